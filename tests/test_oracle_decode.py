@@ -1,0 +1,67 @@
+"""Pins of the oracle's bit-field decoders against library conversions and the OCP tables."""
+import numpy as np
+import torch
+
+from oracle import decode
+
+
+def _same(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape
+    nan_a, nan_b = np.isnan(a), np.isnan(b)
+    assert (nan_a == nan_b).all()
+    ok = ~nan_a
+    assert np.array_equal(a[ok], b[ok])
+    # signed zeros must match too
+    assert np.array_equal(np.signbit(a[ok]), np.signbit(b[ok]))
+
+
+def test_bf16_all_codes():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    _same(decode.bf16(bits), ref)
+
+
+def test_fp16_all_codes():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    _same(decode.fp16(bits), bits.view(np.float16).astype(np.float64))
+
+
+def test_e4m3_all_codes():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    _same(decode.e4m3(b), ref)
+    assert decode.e4m3(np.uint8(0x7E)) == 448.0
+
+
+def test_e8m0_all_codes():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    _same(decode.e8m0(b), ref)
+    assert decode.e8m0(np.uint8(127)) == 1.0
+
+
+def test_e2m1_table():
+    # OCP Microscaling v1.0, FP4 E2M1 element values
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    want = table + [-v for v in table]
+    got = decode.e2m1(np.arange(16))
+    _same(got, want)
+
+
+def test_e2m1_matches_torch_if_available():
+    try:
+        packed = torch.arange(256, dtype=torch.uint8).view(torch.float4_e2m1fn_x2)
+        vals = packed.to(torch.float32)  # may not be supported
+    except Exception:
+        return
+    # torch's unpack order is not documented; check the value multiset only
+    got = np.sort(decode.e2m1(decode.fp4x2_unpack(np.arange(256, dtype=np.uint8)[:, None]).ravel()))
+    assert np.array_equal(np.sort(vals.double().numpy().ravel()), got)
+
+
+def test_fp4x2_unpack_order():
+    # reading: element 2j in the low nibble of byte j
+    codes = decode.fp4x2_unpack(np.array([[0x21, 0xF7]], dtype=np.uint8))
+    assert codes.tolist() == [[1, 2, 7, 15]]

@@ -1,0 +1,216 @@
+"""Pins of the oracle LRU (ensure_experts) and copy_missing.
+
+1. A hand-worked trace (tests/golden/lru_trace_s3_e3.txt).
+2. An independent textbook LRU - a recency list with move-to-MRU, written here
+   without timestamps - must agree step for step with the timestamp oracle on
+   random traces and on every short trace of a tiny pool.
+3. Invariants: every requested id resident afterwards, owners unique, no
+   member of the request evicted, copies == misses, capacity failure leaves the
+   state unchanged, only cold misses when the pool holds every id.
+"""
+import itertools
+import os
+import random
+
+import numpy as np
+import pytest
+
+from oracle import copy as ocopy
+from oracle import formulas
+from oracle.lru import ERR_ARG, ERR_CAPACITY, OK, SlotTable
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ints(s):
+    return [int(v) for v in s.split(",")] if s.strip() not in ("", "-") else None
+
+
+def _rows(s):
+    s = s.strip()
+    return None if s == "-" else [_ints(r) for r in s.split(";")]
+
+
+def test_hand_worked_trace():
+    lines = [l.split("#")[0].strip() for l in open(os.path.join(GOLDEN, "lru_trace_s3_e3.txt"))]
+    lines = [l for l in lines if l]
+    pool = dict(kv.split("=") for kv in lines[0].split()[1:])
+    t = SlotTable(int(pool["S"]), int(pool["L"]), int(pool["E"]))
+    init = dict(kv.split("=") for kv in lines[1].split()[1:])
+    t.set_state(_ints(init["owner"]), _ints(init["stamp"]), int(init["clock"]))
+    for line in lines[2:]:
+        lhs, rhs = line.split("->")
+        _, layer, ids = lhs.split()
+        status, slots, misses, owner, stamp, ev = [p.strip() for p in rhs.split("|")]
+        r = t.ensure(int(layer), _rows(ids))
+        assert r.status == int(status), line
+        if r.status == OK:
+            assert r.slot_ids.tolist() == _rows(slots), line
+            want = [tuple(int(v) for v in m.split(":")) for m in misses.split()]
+            assert r.misses == want, line
+            assert r.evictions == int(ev), line
+        assert t.owner.tolist() == _ints(owner), line
+        assert t.stamp.tolist() == _ints(stamp), line
+
+
+def test_capacity_leaves_state():
+    t = SlotTable(2, 1, 3)
+    before = t.snapshot()
+    r = t.ensure(0, [[0, 1, 2]])
+    assert r.status == ERR_CAPACITY
+    after = t.snapshot()
+    assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+    assert before[2] == after[2]
+    # exactly S distinct ids fit
+    assert t.ensure(0, [[0, 1]]).status == OK
+
+
+def test_arg_errors():
+    t = SlotTable(4, 2, 3)
+    assert t.ensure(2, [[0]]).status == ERR_ARG
+    assert t.ensure(-1, [[0]]).status == ERR_ARG
+    assert t.ensure(0, [[3]]).status == ERR_ARG
+    assert t.ensure(0, [[-1]]).status == ERR_ARG
+
+
+class TextbookLRU:
+    """Recency list (LRU first) with move-to-MRU; no timestamps.
+
+    Batch rule: misses (ascending) take victims from the LRU end, skipping
+    slots that hold requested ids; then the slots of all requested ids move to
+    the MRU end in ascending id order.  Empty slots start at the LRU end.
+    """
+
+    def __init__(self, S, L, E, owner=None, order=None):
+        self.S, self.L, self.E = S, L, E
+        self.owner = list(owner) if owner is not None else [-1] * S
+        self.order = list(order) if order is not None else list(range(S))
+
+    def step(self, layer, ids):
+        flat = [[layer * self.E + e for e in row] for row in ids]
+        U = sorted({f for row in flat for f in row})
+        pos = {o: s for s, o in enumerate(self.owner) if o >= 0}
+        miss = [u for u in U if u not in pos]
+        victims = [s for s in self.order if self.owner[s] not in U]
+        if len(miss) > len(victims):
+            return None
+        installs = []
+        for u, s in zip(miss, victims):
+            self.owner[s] = u
+            pos[u] = s
+            installs.append((s, u))
+        for u in U:
+            self.order.remove(pos[u])
+            self.order.append(pos[u])
+        return [[pos[f] for f in row] for row in flat], installs
+
+
+def _compare_trace(S, L, E, steps):
+    a = SlotTable(S, L, E)
+    b = TextbookLRU(S, L, E)
+    for layer, ids in steps:
+        ra = a.ensure(layer, ids)
+        rb = b.step(layer, ids)
+        if rb is None:
+            assert ra.status == ERR_CAPACITY
+            continue
+        assert ra.status == OK
+        assert ra.slot_ids.tolist() == rb[0]
+        assert ra.misses == rb[1]
+        assert a.owner.tolist() == b.owner
+
+
+def test_random_traces_against_textbook_lru():
+    rng = random.Random(1234)
+    for _ in range(100):
+        L, E, S = rng.randint(1, 3), rng.randint(1, 6), rng.randint(1, 5)
+        steps = []
+        for _ in range(100):
+            n, k = rng.randint(1, 3), rng.randint(1, 2)
+            steps.append((rng.randrange(L), [[rng.randrange(E) for _ in range(k)] for _ in range(n)]))
+        _compare_trace(S, L, E, steps)
+
+
+def test_exhaustive_short_traces():
+    L, E = 2, 3
+    singles = [(l, [[e]]) for l in range(L) for e in range(E)]
+    pairs = [(l, [[e1, e2]]) for l in range(L) for e1 in range(E) for e2 in range(E)]
+    alphabet = singles + pairs
+    for S in (1, 2, 3):
+        for length in (1, 2, 3):
+            for trace in itertools.product(alphabet, repeat=length):
+                _compare_trace(S, L, E, list(trace))
+    # length-4 traces over single requests
+    for S in (1, 2, 3):
+        for trace in itertools.product(singles, repeat=4):
+            _compare_trace(S, L, E, list(trace))
+
+
+def test_invariants_random():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        L, E = int(rng.integers(1, 4)), int(rng.integers(2, 9))
+        S = int(rng.integers(1, 10))
+        t = SlotTable(S, L, E)
+        for _ in range(30):
+            layer = int(rng.integers(L))
+            ids = rng.integers(0, E, size=(int(rng.integers(1, 4)), int(rng.integers(1, 3))))
+            before = t.snapshot()
+            U = sorted(set((layer * E + ids).ravel().tolist()))
+            r = t.ensure(layer, ids)
+            if r.status == ERR_CAPACITY:
+                assert len(U) > S
+                assert np.array_equal(before[0], t.owner) and np.array_equal(before[1], t.stamp)
+                continue
+            assert r.status == OK
+            owners = [o for o in t.owner.tolist() if o >= 0]
+            assert len(owners) == len(set(owners))
+            for u in U:
+                assert u in owners
+            # requested ids that were resident stayed in their slots
+            for s, o in enumerate(before[0].tolist()):
+                if o in U:
+                    assert t.owner[s] == o
+            assert len(r.misses) == len(U) - r.hits
+            assert np.array_equal(t.owner[r.slot_ids], layer * E + ids)
+
+
+def test_only_cold_misses_when_pool_holds_everything():
+    L, E = 2, 4
+    t = SlotTable(L * E, L, E)
+    seen = set()
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        layer = int(rng.integers(L))
+        ids = rng.integers(0, E, size=(2, 2))
+        flat = set((layer * E + ids).ravel().tolist())
+        r = t.ensure(layer, ids)
+        assert {m[1] for m in r.misses} == flat - seen
+        seen |= flat
+
+
+def test_copy_missing_moves_rows_and_keeps_sentinel():
+    E, S = 5, 4
+    rng = np.random.default_rng(0)
+    row_bytes = [32, 16]
+    host = [[rng.integers(0, 256, size=(E, rb), dtype=np.uint8)] for rb in row_bytes]
+    slots = [np.full((S, rb), 0xA5, dtype=np.uint8) for rb in row_bytes]
+    t = SlotTable(S, 1, E)
+    r = t.ensure(0, [[4, 1]])
+    moved = ocopy.copy_missing(r.misses, host, slots, E)
+    assert moved == 2 * sum(row_bytes)
+    touched = {s for s, _ in r.misses}
+    for b in range(2):
+        for s in range(S):
+            if s in touched:
+                fid = dict(r.misses)[s]
+                assert np.array_equal(slots[b][s], host[b][0][fid])
+            else:
+                assert (slots[b][s] == 0xA5).all()
+
+
+def test_zero_and_full_miss_rate():
+    E, S, n, k = 16, 8, 4, 2
+    active = formulas.active_unique(n, k, E)
+    assert formulas.num_misses(active, 0.0) == 0
+    assert formulas.num_misses(active, 1.0) == active
