@@ -1,0 +1,297 @@
+"""Benchmark of the per-layer offloaded-expert MoE step on one MI355X.
+
+Metric: copy_missing GB/s + tok_ms per miss rate; MoE-layer decode tok/s at bs=1.
+
+Workload (default): bf16 banks, H=2048, I=768, E=128 experts, top-8, L=48
+MoE layers, a 1024-slot pool whose every slot starts owned by another layer;
+layer 0 is driven and per-token costs are extrapolated over L layers (FreeToken
+MoE benchmark guide §4.3-§4.4).  Inputs are seeded synthetic tensors resident
+in HBM (activations, router) and in pinned host banks (experts).
+
+One "step" = route -> ensure_experts -> copy_missing -> expert_ffn for one
+token (bs=1), with the slot table reset (untimed) before each step so that
+misses = round(active * miss_rate) of the routed experts miss.  Each step is
+timed with HIP events on the launch stream; value = 1000 / (L * ms_per_step).
+
+Also printed (same JSON line): the copy sweep of the benchmark guide's columns
+(bs, active, miss_rate, misses, time_ms, copy_MiB, bw_GBps, tok_ms; median of
+25 event-timed ensure+copy repeats, fused and per-bank), decode tok/s at every
+miss rate, the measured ceilings (pinned H2D by DMA and by the zero-copy
+kernel, HBM streaming read), the roofline of the dominant kernel and of the
+FFN, and the CPU oracle timed on this host.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "copy_missing GB/s + tok_ms per miss rate; MoE-layer decode tok/s at bs=1"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+PCIE_PEAK_GBS = 64.0         # PCIe 5.0 x16, one direction, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=25)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_h2048")
+    ap.add_argument("--miss-rate", type=float, default=0.5)
+    ap.add_argument("--repeat", type=int, default=25, help="repeats per copy-sweep row (median)")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the step has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import offloaded_expert_slot_amd as oes
+    import synth
+    from synth.workloads import WORKLOADS, make_host_banks
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+
+    t0 = time.time()
+    hb = make_host_banks(w)
+    log(f"host banks ready ({sum(b.numel() for b in hb.banks) / 2**30:.2f} GiB pinned) in {time.time() - t0:.1f}s")
+    sc = oes.schema_make(w.fmt, w.L, w.E, w.H, w.I)
+    bpe = sc.bytes_per_expert
+    cache = oes.Cache(sc, w.S, 0)
+    for b, t in enumerate(hb.banks):
+        cache.set_source(b, 0, t)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---------------------------------------------------------------- ceilings
+    probes = {}
+    if not args.no_probes:
+        src = hb.banks[0]
+        nbytes = (src.numel() // 16) * 16
+        dbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dma = [oes.probe_h2d_dma(dbuf, src, nbytes) for _ in range(5)]
+        zc = [oes.probe_h2d_kernel(dbuf, src, nbytes, 1024) for _ in range(5)]
+        big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+        big.fill_(1)
+        sink = torch.zeros(4, dtype=torch.float32, device=dev)
+        hbm = [oes.probe_hbm_read(big, big.numel(), sink) for _ in range(5)]
+        probes = {
+            "h2d_dma_GBps": nbytes / (min(dma) * 1e6),
+            "h2d_zero_copy_GBps": nbytes / (min(zc) * 1e6),
+            "hbm_read_GBps": big.numel() / (min(hbm) * 1e6),
+            "h2d_bytes": nbytes,
+        }
+        probes["h2d_peak_GBps"] = max(probes["h2d_dma_GBps"], probes["h2d_zero_copy_GBps"])
+        del big, dbuf
+        log("probes", {k: round(v, 1) for k, v in probes.items()})
+
+    # ---------------------------------------------------------------- decode step at bs=1
+    n = 1
+    x = synth.activations(n, w.H, 0, w.name).to(dev)
+    wg = synth.router_weight(w.H, w.E, 0, w.name).to(dev)
+    ids = torch.empty((n, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((n, w.k), dtype=torch.float32, device=dev)
+    slot_ids = torch.empty_like(ids)
+    y = torch.empty((n, w.H), dtype=torch.int16, device=dev)
+    rws = torch.empty(oes.route_workspace_bytes(n, w.H, w.E), dtype=torch.uint8, device=dev)
+    fws = torch.empty(cache.ffn_workspace_bytes(n, w.k), dtype=torch.uint8, device=dev)
+    oes.route(x, wg, w.k, ids, wts, rws)
+    torch.cuda.synchronize()
+    routed = ids.cpu().numpy()
+    active = len(set(routed.ravel().tolist()))
+    u_bytes = active * bpe
+
+    def prepare(mr):
+        misses = int(round(active * mr))
+        owner, stamp, clock, pre = synth.forced_miss_state(w.S, w.E, 0, routed, misses)
+        return misses, owner, stamp, clock, pre
+
+    def run_steps(mr, steps, warmup):
+        misses, owner, stamp, clock, pre = prepare(mr)
+        cache.set_state(owner, stamp, clock)
+        if pre:
+            cache.load_rows([p[0] for p in pre], [p[1] for p in pre])
+        rec = []
+        for i in range(warmup + steps):
+            cache.set_state(owner, stamp, clock)
+            torch.cuda.synchronize()
+            e = [ev() for _ in range(5)]
+            e[0].record(stream)
+            oes.route(x, wg, w.k, ids, wts, rws)
+            e[1].record(stream)
+            cache.ensure_experts(0, ids, slot_ids)
+            e[2].record(stream)
+            cache.copy_missing()
+            e[3].record(stream)
+            cache.expert_ffn(x, slot_ids, wts, y, fws)
+            e[4].record(stream)
+            if i >= warmup:
+                rec.append(e)
+        torch.cuda.synchronize()
+        cache.check()
+        parts = np.array([[r[j].elapsed_time(r[j + 1]) for j in range(4)] for r in rec])
+        total = np.array([r[0].elapsed_time(r[4]) for r in rec])
+        return misses, total, parts
+
+    per_mr = []
+    headline = None
+    for mr in sorted(set(w.miss_rates) | {args.miss_rate}):
+        is_head = abs(mr - args.miss_rate) < 1e-12
+        steps = args.steps if is_head else max(5, args.steps // 3)
+        misses, total, parts = run_steps(mr, steps, args.warmup if is_head else 2)
+        ms = float(total.mean())
+        row = {"miss_rate": mr, "misses": misses, "ms_per_step": ms, "ms_median": float(np.median(total)),
+               "tok_ms": ms * w.L, "decode_tok_s": 1000.0 / (w.L * ms),
+               "route_ms": float(parts[:, 0].mean()), "ensure_ms": float(parts[:, 1].mean()),
+               "copy_ms": float(parts[:, 2].mean()), "ffn_ms": float(parts[:, 3].mean())}
+        if misses:
+            row["copy_GBps"] = misses * bpe / (row["copy_ms"] * 1e6)
+        per_mr.append(row)
+        if is_head:
+            headline = (row, total, parts)
+        log("decode", {k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()})
+
+    # ---------------------------------------------------------------- copy sweep
+    sweep = []
+    if not args.no_sweep:
+        for bs in w.batches:
+            sids = synth.synthetic_ids(bs, w.k, w.E, 0, w.name)
+            d_ids = sids.to(dev)
+            d_slots = torch.empty_like(d_ids)
+            act = min(w.E, bs * w.k)
+            for mr in w.miss_rates:
+                m = int(round(act * mr))
+                owner, stamp, clock, _ = synth.forced_miss_state(w.S, w.E, 0, sids.numpy(), m)
+                row = {"bs": bs, "active": act, "miss_rate": mr, "misses": m}
+                for fused in (1, 0):
+                    cache.set_option(oes.OPT_FUSED_COPY, fused)
+                    times = []
+                    for _ in range(args.repeat):
+                        cache.set_state(owner, stamp, clock)
+                        torch.cuda.synchronize()
+                        a, b = ev(), ev()
+                        a.record(stream)
+                        cache.ensure_experts(0, d_ids, d_slots)
+                        cache.copy_missing()
+                        b.record(stream)
+                        b.synchronize()
+                        times.append(a.elapsed_time(b))
+                    tm = statistics.median(times)
+                    key = "" if fused else "_per_bank"
+                    row["time_ms" + key] = tm
+                    row["bw_GBps" + key] = (m * bpe / (tm * 1e6)) if m else None
+                row["copy_MiB"] = m * bpe / 2**20
+                row["tok_ms"] = row["time_ms"] * w.L
+                if probes and row["bw_GBps"]:
+                    row["frac_h2d_peak"] = row["bw_GBps"] / probes["h2d_peak_GBps"]
+                sweep.append(row)
+                log("sweep", {k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()})
+        cache.set_option(oes.OPT_FUSED_COPY, 1)
+        cache.check()
+
+    # ---------------------------------------------------------------- rooflines
+    head, total, parts = headline
+    ffn_row = next(r for r in per_mr if r["misses"] == 0) if any(r["misses"] == 0 for r in per_mr) else head
+    ffn_gbs = u_bytes / (ffn_row["ffn_ms"] * 1e6)
+    kernels = {
+        "expert_ffn": {"bound": "hbm", "achieved": ffn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": ffn_gbs / HBM_PEAK_GBS, "bytes_per_launch": u_bytes,
+                       "avg_ms": ffn_row["ffn_ms"], "traffic": None},
+    }
+    if head["misses"]:
+        cbytes = head["misses"] * bpe
+        cgbs = cbytes / (head["copy_ms"] * 1e6)
+        kernels["copy_missing"] = {"bound": "host_link", "achieved": cgbs, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                                   "frac": cgbs / PCIE_PEAK_GBS, "bytes_per_launch": cbytes,
+                                   "avg_ms": head["copy_ms"], "traffic": None}
+        if probes:
+            kernels["copy_missing"]["frac_of_measured_h2d_peak"] = cgbs / probes["h2d_peak_GBps"]
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    roof = dict(kernels[dominant])
+    roof = {"kernel": dominant, "bound": roof["bound"], "achieved": roof["achieved"], "peak": roof["peak"],
+            "unit": roof["unit"], "frac": roof["frac"], "traffic": roof["traffic"]}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(w, hb, x, wg, args.miss_rate, args.cpu_seconds)
+        log("cpu_baseline", cpu)
+
+    ms = head["ms_per_step"]
+    out = {
+        "metric": METRIC, "value": 1000.0 / (w.L * ms), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "format": w.fmt, "hidden": w.H, "inter": w.I, "experts": w.E,
+                   "topk": w.k, "layers": w.L, "slots": w.S, "bs": 1, "miss_rate": args.miss_rate,
+                   "misses": head["misses"], "active": active, "bytes_per_expert": bpe},
+        "tok_ms": head["tok_ms"], "copy_GBps": head.get("copy_GBps"),
+        "roofline": roof, "kernels": kernels, "probes": probes, "decode_per_miss_rate": per_mr,
+        "copy_sweep": sweep, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    cache.close()
+
+
+def _cpu_baseline(w, hb, x, wg, mr, budget_s):
+    """The oracle, as it stands, on this host: route + LRU + row copies + FFN for bs=1 steps."""
+    import numpy as np
+
+    import synth
+    from oracle import copy as ocopy
+    from oracle import ffn as offn
+    from oracle import route as oroute
+    from oracle.lru import SlotTable
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    xb = x.cpu().numpy().view(np.uint16)
+    wgb = wg.cpu().numpy().view(np.uint16)
+    host = [[hb.banks[b].numpy().reshape(w.E, -1)] for b in range(len(hb.banks))]
+    mirror = [np.zeros((w.S, rb), dtype=np.uint8) for rb in hb.row_bytes]
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 25):
+        t0 = time.perf_counter()
+        ids, wts, _ = oroute.route(xb, wgb, w.k)
+        active = len(set(ids.ravel().tolist()))
+        owner, stamp, clock, pre = synth.forced_miss_state(w.S, w.E, 0, ids, int(round(active * mr)))
+        t = SlotTable(w.S, w.L, w.E)
+        t.set_state(owner, stamp, clock)
+        t1 = time.perf_counter()
+        r = t.ensure(0, ids)
+        ocopy.copy_missing(r.misses, host, mirror, w.E)
+        offn.expert_ffn(w.fmt, w.H, w.I, xb, r.slot_ids, wts,
+                        lambda s: [host[b][0][int(t.owner[s]) % w.E] for b in range(len(host))])
+        t2 = time.perf_counter()
+        times.append(((t2 - t1) + (t1 - t0)) * 1000.0)
+    ms = float(np.median(times))
+    return {"value": 1000.0 / (w.L * ms), "unit": "tok/s", "cores": int(blas_threads), "kind": "oracle",
+            "ms_per_step": ms, "sample": f"{len(times)} bs=1 decode steps of {w.name} at miss_rate {mr} "
+                                        f"(route, LRU, row copies, float64 FFN), median",
+            "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

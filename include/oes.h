@@ -1,0 +1,313 @@
+/*
+ * oes.h - C ABI of liboes.so: offloaded expert slots on an MI355X (gfx950).
+ *
+ * The per-layer MoE expert step of an offloaded-expert inference engine:
+ *
+ *   route -> ensure_experts -> copy_missing -> expert_ffn
+ *
+ * Expert weights live in caller-owned pinned host memory as "banks", one bank
+ * per schema tensor, each bank supplied as one host tensor per layer; the GPU
+ * keeps one slot cache shared by every layer; each step remaps the routed
+ * experts (flat id = layer * E + expert) onto slots with a global LRU, gathers
+ * the missing experts' rows from every bank in one fused copy, and runs the
+ * SwiGLU expert FFN on the slot cache.  (FreeToken architecture walk-through
+ * §5; FreeToken MoE benchmark guide §1 background, §4.1-§4.4.)  Prefill
+ * streams whole layers through a two-deep device buffer so copy and compute
+ * overlap (architecture walk-through §5).
+ *
+ * Conventions for every function:
+ *   - returns oes_status: OES_OK (0) or a negative error; never throws, never
+ *     aborts; on error oes_last_error() holds a thread-local message;
+ *   - argument errors are detected before any GPU work and change no state;
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream);
+ *     step calls only enqueue work on it and never synchronise; calls that
+ *     return device-side results to the host say "syncs" and synchronise it;
+ *   - device pointers are plain device addresses (e.g. torch tensor data);
+ *     host pointers are plain host addresses;
+ *   - a cache is not thread-safe: use it from one thread and one stream.
+ *
+ * Weights use the [out, in] convention: gate_up is [2I, H] (rows [0, I) gate,
+ * rows [I, 2I) up) and down is [H, I]; activations are bf16 [n, H] row-major.
+ */
+#ifndef OES_H_
+#define OES_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OES_ABI_VERSION 1
+
+typedef int32_t oes_status;
+enum {
+  OES_OK = 0,
+  OES_ERR_ARG = -1,         /* bad argument; nothing done */
+  OES_ERR_CAPACITY = -2,    /* more distinct experts in a step than slots */
+  OES_ERR_HIP = -3,         /* a HIP runtime call failed (message has hipGetErrorString) */
+  OES_ERR_NOMEM = -4,       /* device or host allocation failed */
+  OES_ERR_STATE = -5,       /* call not valid in the object's current state */
+  OES_ERR_UNSUPPORTED = -6  /* format / size combination not implemented */
+};
+
+/* Static string for a status code. */
+const char *oes_status_str(oes_status s);
+/* Thread-local detail message of the last failing call on this thread ("" if none). */
+const char *oes_last_error(void);
+/* OES_ABI_VERSION of the loaded library. */
+int32_t oes_abi_version(void);
+
+/* ------------------------------------------------------------------ schema */
+/*
+ * Bank schema (FreeToken MoE benchmark guide §4.2; architecture walk-through
+ * §5): every format declares its own list of banks, one row per expert per
+ * bank; the cache moves rows and does not care about their layout.
+ *
+ *   OES_BF16          gate_up [2I,H] bf16, down [H,I] bf16
+ *   OES_FP8_BLOCK128  gate_up [2I,H] e4m3, gate_up_scale [2I/128,H/128] f32,
+ *                     down [H,I] e4m3, down_scale [H/128,I/128] f32
+ *                     (W = e4m3(q) * scale of its 128x128 block)
+ *   OES_NVFP4         gate_up_codes [2I,H/2] (two e2m1 per byte, element 2j in
+ *                     the low nibble), gate_up_scale [2I,H/16] e4m3,
+ *                     gate_up_global [2I] fp16, then the same three for down
+ *                     (W = e2m1 * e4m3 scale of its 16-block * fp16 row global)
+ *   OES_MXFP4_T       gate_up_blocks [H/32,2I,16] u8 (32 e2m1 codes along K per
+ *                     16 bytes), gate_up_scales [H/32,2I] e8m0, gate_up_bias
+ *                     [2I] bf16, then the same three for down over [I/32,H,16]
+ *                     (W[n,c] = e2m1 * 2^(scale-127); bias added after the matmul)
+ */
+enum { OES_BF16 = 0, OES_FP8_BLOCK128 = 1, OES_NVFP4 = 2, OES_MXFP4_T = 3 };
+enum {
+  OES_ELEM_BF16 = 0, OES_ELEM_E4M3 = 1, OES_ELEM_F32 = 2, OES_ELEM_FP4X2 = 3,
+  OES_ELEM_FP16 = 4, OES_ELEM_E8M0 = 5, OES_ELEM_U8 = 6
+};
+#define OES_MAX_BANKS 6
+#define OES_MAX_SLOTS 4096     /* slot pool limit of the single-workgroup remap */
+#define OES_MAX_EXPERTS 4096   /* experts per layer */
+
+typedef struct {
+  char name[24];        /* e.g. "gate_up_codes" */
+  int32_t elem;         /* OES_ELEM_* */
+  int32_t ndim;         /* 1..3 */
+  int64_t shape[3];     /* row shape; for FP4X2 the last dim counts bytes */
+  int64_t row_bytes;    /* bytes of one expert's row (always a multiple of 16) */
+} oes_bank_spec;
+
+typedef struct {
+  int32_t format, num_layers, num_experts, hidden, inter, num_banks;
+  oes_bank_spec bank[OES_MAX_BANKS];
+  int64_t bytes_per_expert;  /* sum of row_bytes over the banks */
+} oes_schema;
+
+/* Fill *out with the bank list of a format (the pages' bank_specs()).
+ * Errors: OES_ERR_ARG for L, E, H, I <= 0, E > OES_MAX_EXPERTS, sizes the
+ * format cannot tile (bf16: H, I multiples of 8; fp8: of 128; nvfp4: of 32;
+ * mxfp4: of 32), or an unknown format.  Pure host code, no GPU needed. */
+oes_status oes_schema_make(int32_t format, int32_t num_layers, int32_t num_experts,
+                           int32_t hidden, int32_t inter, oes_schema *out);
+
+/* ------------------------------------------------------------------ slot cache */
+typedef struct oes_cache oes_cache;
+
+typedef struct {
+  uint64_t steps;         /* successful ensure_experts calls */
+  uint64_t hits;          /* distinct requested ids already resident */
+  uint64_t misses;        /* distinct requested ids installed */
+  uint64_t evictions;     /* misses that displaced a non-empty slot */
+  uint64_t bytes_copied;  /* misses * bytes_per_expert */
+  uint32_t last_misses;   /* misses of the last successful step */
+  int32_t failed_steps;   /* ensure_experts calls that failed on the device */
+} oes_stats;
+
+/* Create a slot cache of num_slots experts on HIP device `device`
+ * (architecture walk-through §5; benchmark guide §1: one unified slot cache).
+ * The cache owns: one HBM slot bank per schema bank (num_slots rows each), the
+ * slot table (owner int64 = flat id or -1, stamp uint64, a clock), the miss
+ * list and a device status word.  Initial state: every slot empty, stamps 0,
+ * clock 0; slot bytes are undefined until written.
+ * Errors: OES_ERR_ARG (null, num_slots < 1 or > OES_MAX_SLOTS, bad schema),
+ * OES_ERR_NOMEM, OES_ERR_HIP. */
+oes_status oes_cache_create(const oes_schema *schema, int32_t num_slots, int32_t device,
+                            oes_cache **out);
+/* Free everything the cache owns (after synchronising its device).  NULL is OK. */
+oes_status oes_cache_destroy(oes_cache *c);
+
+/* Register the host tensor holding bank `bank` of layer `layer`: E rows of
+ * row_bytes each, contiguous, expert-major (benchmark guide §4.4: each bank's
+ * sources are a per-layer list).  `host` must be pinned host memory the
+ * device can read (hipHostMalloc / torch pin_memory), 16-byte aligned, and
+ * must outlive the cache; it stays caller-owned.  bytes must equal
+ * E * row_bytes.  Errors: OES_ERR_ARG (range, size, alignment, memory that is
+ * not pinned host memory), OES_ERR_HIP. */
+oes_status oes_cache_set_source(oes_cache *c, int32_t bank, int32_t layer, const void *host,
+                                int64_t bytes);
+
+/* Overwrite the slot table (the benchmark's prepare_state, benchmark guide
+ * §4.3) from host arrays of num_slots entries; clears the device status and
+ * miss list.  owner[s] must be -1 or in [0, 2^50); stamp[s] < 2^62 and
+ * clock < 2^62.  Enqueued on `stream` (host arrays are copied before return). */
+oes_status oes_cache_set_state(oes_cache *c, const int64_t *owner, const uint64_t *stamp,
+                               uint64_t clock, void *stream);
+/* Read the slot table into host arrays of num_slots entries (any pointer may
+ * be NULL).  Syncs `stream`. */
+oes_status oes_cache_get_state(oes_cache *c, int64_t *owner, uint64_t *stamp, uint64_t *clock,
+                               void *stream);
+
+/* Copy the rows of flat ids ids[i] into slots slots[i] from the registered
+ * sources (host arrays of `count` entries), without touching the slot table:
+ * used to warm slots whose owners were set by oes_cache_set_state.  Same copy
+ * kernel as copy_missing.  Errors: OES_ERR_ARG (range, missing source). */
+oes_status oes_cache_load_rows(oes_cache *c, const int32_t *slots, const int64_t *ids,
+                               int32_t count, void *stream);
+
+/* Fill every byte of every slot bank with `value` (test sentinel). */
+oes_status oes_cache_fill_slots(oes_cache *c, uint8_t value, void *stream);
+
+/* Device base address and row bytes of slot bank `bank` (row s at base + s*row_bytes). */
+oes_status oes_cache_slot_bank(const oes_cache *c, int32_t bank, void **dev_base,
+                               int64_t *row_bytes);
+/* Number of slots, and the cache's schema. */
+oes_status oes_cache_info(const oes_cache *c, int32_t *num_slots, oes_schema *schema);
+
+/* Miss list of the last ensure_experts: *count entries (slot, flat id) in
+ * install order (ascending id).  Copies at most `cap` entries.  Syncs. */
+oes_status oes_cache_get_misses(oes_cache *c, int32_t *count, int32_t *slots, int64_t *ids,
+                                int32_t cap, void *stream);
+/* Counters since creation.  Syncs. */
+oes_status oes_cache_stats(oes_cache *c, oes_stats *out, void *stream);
+/* Syncs `stream`, then returns and clears the sticky device error: OES_OK,
+ * OES_ERR_CAPACITY (a step requested more distinct experts than slots) or
+ * OES_ERR_ARG (a step held an id outside [0, E)). */
+oes_status oes_cache_check(oes_cache *c, void *stream);
+
+/* Options.  OES_OPT_FUSED_COPY: 1 (default) one launch gathers every bank;
+ * 0 one launch per bank (the A/B path; default taken from env OES_FUSED_COPY
+ * at creation).  OES_OPT_COPY_MODE: OES_COPY_ZERO (default) the gather
+ * kernel reads mapped pinned memory; OES_COPY_SDMA copy_missing syncs the
+ * stream, reads the miss list and issues one DMA copy per (miss, bank)
+ * (default from env OES_COPY_MODE=zerocopy|sdma). */
+enum { OES_OPT_FUSED_COPY = 1, OES_OPT_COPY_MODE = 2, OES_OPT_COPY_BLOCKS = 3 };
+enum { OES_COPY_ZERO = 0, OES_COPY_SDMA = 1 };
+oes_status oes_cache_set_option(oes_cache *c, int32_t option, int64_t value);
+
+/* ------------------------------------------------------------------ the step */
+
+/* Router workspace bytes for n tokens, H hidden, E experts. */
+oes_status oes_route_workspace(int32_t n, int32_t hidden, int32_t num_experts, int64_t *bytes);
+
+/* Top-k routing: logits = x . Wg (bf16 inputs, fp32 sums), softmax over the E
+ * experts, the k largest in descending order (equal logits: lower expert
+ * first), weights renormalised to sum to 1 (the top-k of each MoE layer;
+ * benchmark guide §4.3 routes bs * topk experts per step).
+ *   x   [n, H] bf16 device, wg [H, E] bf16 device (row-major)
+ *   ids [n, k] int32 device out, w [n, k] float device out
+ *   logits [n, E] float device out, or NULL
+ *   workspace: device, >= oes_route_workspace bytes, 16-byte aligned.
+ * Limits: 1 <= k <= min(E, 32), E even and <= 512, n >= 0. */
+oes_status oes_route(const void *x, const void *wg, int32_t n, int32_t hidden,
+                     int32_t num_experts, int32_t k, int32_t *ids, float *w, float *logits,
+                     void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Top-k of given router logits [n, E] float device (prefill routes given logits). */
+oes_status oes_route_logits(const float *logits, int32_t n, int32_t num_experts, int32_t k,
+                            int32_t *ids, float *w, void *stream);
+
+/* ensure_experts: global LRU remap of layer `layer`'s routed experts onto the
+ * slot pool (benchmark guide §4.1, §4.3; architecture walk-through §5).
+ *   ids [n, k] int32 device (expert index within the layer), slot_ids [n, k]
+ *   int32 device out.
+ * One workgroup does the whole remap on the device:
+ *   U = sorted distinct flat ids layer*E + ids; resident ones are hits; the
+ *   others are installed in ascending id order into the evictable slots (those
+ *   not holding a member of U) ordered by (not empty, stamp, owner, slot);
+ *   the clock advances and every slot holding a member of U is stamped; the
+ *   miss list (slot, id) is kept for copy_missing; slot_ids[t, j] is the slot
+ *   of ids[t, j].
+ * Device-side failures (an id outside [0, E): OES_ERR_ARG; |U| > num_slots:
+ * OES_ERR_CAPACITY) leave the slot table unchanged, write -1 to slot_ids,
+ * empty the miss list, make the following copy_missing / expert_ffn of this
+ * step no-ops, and are reported by the next syncing call (oes_cache_check).
+ * Host-side errors: layer outside [0, L), n*k < 0 or > 65536, k < 1.
+ * Async. */
+oes_status oes_ensure_experts(oes_cache *c, int32_t layer, const int32_t *ids, int32_t n,
+                              int32_t k, int32_t *slot_ids, void *stream);
+
+/* copy_missing: for every (slot, flat id) of the last miss list and every bank
+ * b, copy row id % E of layer id / E's host bank b into slot row `slot` of
+ * slot bank b (benchmark guide §4.1, §4.4: a per-bank index gather, fused
+ * across banks in one launch).  Async (zero-copy mode).  A miss whose layer
+ * has no registered source for some bank is skipped and sets OES_ERR_ARG in
+ * the sticky status. */
+oes_status oes_copy_missing(oes_cache *c, void *stream);
+
+/* Workspace bytes expert_ffn needs for n tokens with top-k. */
+oes_status oes_expert_ffn_workspace(const oes_cache *c, int32_t n, int32_t k, int64_t *bytes);
+
+/* expert_ffn: y[t] = sum_j w[t, j] * (Wd . (silu(Wg . x_t) * (Wu . x_t)))
+ * computed on slot slot_ids[t, j] of the slot cache (architecture walk-through
+ * §5: hits are computed from the slot cache).  Quantised banks are dequantised
+ * in registers; sums are fp32; y is bf16 (round to nearest even).
+ *   x [n, H] bf16 device, slot_ids [n, k] int32 device (-1 = skip the pair),
+ *   w [n, k] float device, y [n, H] bf16 device out, workspace device.
+ * Formats: OES_BF16, OES_FP8_BLOCK128, OES_NVFP4 (decode).  Limits:
+ * n * k <= 65536, k <= 32.  A no-op when the last ensure_experts failed on the
+ * device.  Async. */
+oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
+                          int32_t n, int32_t k, void *y, void *workspace, int64_t workspace_bytes,
+                          void *stream);
+
+/* ------------------------------------------------------------------ prefill layer streaming */
+/*
+ * Whole-layer double-buffered streaming for prefill (architecture walk-through
+ * §5): `depth` device buffers each hold every expert of one layer (row e =
+ * expert e) for every bank.  oes_layers_prefetch copies layer l's host banks
+ * into buffer l % depth on a copy stream with DMA and records an event;
+ * oes_layers_ffn makes the compute stream wait for that event, runs the
+ * grouped expert FFN of the layer on that buffer, and records a release event
+ * the next prefetch into the same buffer waits for.
+ */
+typedef struct oes_layers oes_layers;
+
+oes_status oes_layers_create(const oes_schema *schema, int32_t depth, int32_t device,
+                             oes_layers **out);
+oes_status oes_layers_destroy(oes_layers *p);
+/* Same contract as oes_cache_set_source. */
+oes_status oes_layers_set_source(oes_layers *p, int32_t bank, int32_t layer, const void *host,
+                                 int64_t bytes);
+/* Enqueue the copy of layer `layer` into buffer layer % depth on copy_stream. */
+oes_status oes_layers_prefetch(oes_layers *p, int32_t layer, void *copy_stream);
+/* Device address and bytes of bank `bank` in buffer `index`. */
+oes_status oes_layers_buffer(const oes_layers *p, int32_t index, int32_t bank, void **dev,
+                             int64_t *bytes);
+/* Workspace bytes oes_layers_ffn needs for n tokens with top-k. */
+oes_status oes_layers_ffn_workspace(const oes_layers *p, int32_t n, int32_t k, int64_t *bytes);
+/* Grouped expert FFN of layer `layer` (which must have been prefetched) over
+ * n tokens routed to ids [n, k] int32 device with weights w [n, k] float
+ * device: y [n, H] bf16.  Format: OES_MXFP4_T (MFMA grouped GEMM).  Async. */
+oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x, const int32_t *ids,
+                          const float *w, int32_t n, int32_t k, void *y, void *workspace,
+                          int64_t workspace_bytes, void *compute_stream);
+
+/* ------------------------------------------------------------------ measurement probes */
+/* Ceilings the benchmark divides by.  All sync and return times in ms.
+ * oes_probe_h2d_dma: one hipMemcpyAsync of `bytes` from pinned host to device.
+ * oes_probe_h2d_kernel: the gather kernel's read of `bytes` of mapped pinned
+ *   host memory into device memory (the zero-copy path's ceiling).
+ * oes_probe_hbm_read: a streaming read of `bytes` of device memory. */
+oes_status oes_probe_h2d_dma(void *dev, const void *host, int64_t bytes, void *stream, float *ms);
+oes_status oes_probe_h2d_kernel(void *dev, const void *host, int64_t bytes, int32_t blocks,
+                                void *stream, float *ms);
+oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, void *sink, void *stream, float *ms);
+
+/* ------------------------------------------------------------------ decoder check */
+/* Decode `n` elements of type `elem` (OES_ELEM_E4M3, OES_ELEM_FP4X2,
+ * OES_ELEM_E8M0, OES_ELEM_BF16, OES_ELEM_FP16) from device `codes` into device
+ * float `out` with the same device routines the FFN kernels use (FP4X2: two
+ * elements per byte, element 2j in the low nibble).  Async.  For tests. */
+oes_status oes_debug_decode(int32_t elem, const void *codes, int32_t n, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OES_H_ */

@@ -1,0 +1,135 @@
+// copy_missing on the device: one launch gathers every missing expert's rows from
+// every bank, reading mapped pinned host memory directly over the host link.
+//
+// FreeToken MoE benchmark guide §4.1 and §4.4: a per-bank index gather of the
+// missing rows, fused across banks into one copy; FreeToken architecture
+// walk-through §6: zero-copy access to pinned host tensors.
+//
+// Work decomposition: every (miss, bank) row is cut into chunks of COPY_CHUNK
+// bytes (64 lanes x 16 B x COPY_UNROLL); the chunks of all misses form one flat
+// index space that the waves of a persistent grid stride over.  A wave issues
+// all COPY_UNROLL 16-byte loads of its chunk before the first store, so each
+// wave keeps COPY_CHUNK bytes of host reads in flight, and writes the slot rows
+// with non-temporal stores (the rows are read back much later by the FFN).
+//
+// The list length lives on the device (the remap kernel wrote it), so the grid
+// is sized for the largest possible list and idle waves exit at once.
+
+#include <algorithm>
+
+#include "oes_internal.h"
+
+namespace oes {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void gather_kernel(CopyArgs a) {
+  if (a.gate && *a.gate == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t total = (int64_t)(*a.count) * a.chunks_per_miss;
+  for (int64_t c = gwave; c < total; c += nwaves) {
+    const int i = (int)(c / a.chunks_per_miss);
+    const int r = (int)(c - (int64_t)i * a.chunks_per_miss);
+    int b = 0;
+#pragma unroll
+    for (int q = 1; q < OES_MAX_BANKS; ++q)
+      if (q < a.nb && r >= a.bank[q].chunk_prefix) b = q;
+    const CopyBank &bk = a.bank[b];
+    const int64_t id = a.id_list[i];
+    const int slot = a.slot_list[i];
+    const int layer = (int)(id / a.E);
+    const int64_t e = id - (int64_t)layer * a.E;
+    const uint64_t src_base = a.src_table[(int64_t)bk.table_col * a.L + layer];
+    if (src_base == 0) {
+      if (lane == 0) atomicCAS(a.err, 0, (int)OES_ERR_ARG);
+      continue;
+    }
+    const int64_t off = (int64_t)(r - bk.chunk_prefix) * COPY_CHUNK;
+    const int64_t nbytes = min(COPY_CHUNK, bk.row_bytes - off);
+    const int n16 = (int)(nbytes >> 4);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(src_base + (uint64_t)(e * bk.row_bytes + off));
+    u32x4 *dst = reinterpret_cast<u32x4 *>(bk.slot_base + (int64_t)slot * bk.row_bytes + off);
+    u32x4 v[COPY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) {
+      const int idx = u * 64 + lane;
+      if (idx < n16) v[u] = src[idx];
+    }
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) {
+      const int idx = u * 64 + lane;
+      if (idx < n16) __builtin_nontemporal_store(v[u], dst + idx);
+    }
+  }
+}
+
+// Linear copy of a mapped host buffer to device memory, same inner loop as the gather.
+__global__ __launch_bounds__(256) void stream_copy_kernel(uint8_t *dst, const uint8_t *src, int64_t bytes) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t chunks = (bytes + COPY_CHUNK - 1) / COPY_CHUNK;
+  for (int64_t c = gwave; c < chunks; c += nwaves) {
+    const int64_t off = c * COPY_CHUNK;
+    const int n16 = (int)(min(COPY_CHUNK, bytes - off) >> 4);
+    const u32x4 *s = reinterpret_cast<const u32x4 *>(src + off);
+    u32x4 *d = reinterpret_cast<u32x4 *>(dst + off);
+    u32x4 v[COPY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) {
+      const int idx = u * 64 + lane;
+      if (idx < n16) v[u] = s[idx];
+    }
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) {
+      const int idx = u * 64 + lane;
+      if (idx < n16) __builtin_nontemporal_store(v[u], d + idx);
+    }
+  }
+}
+
+// Streaming read of device memory: every byte is loaded once, folded into a sum
+// that is written only if it equals an impossible value (keeps the loads alive).
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4 *src, int64_t n16, float *sink) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  int64_t i = tid;
+  for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + nthreads);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * nthreads);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * nthreads);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += nthreads) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x7f3a9e11u) sink[0] = (float)acc;
+}
+
+}  // namespace
+
+hipError_t launch_gather(const CopyArgs &a, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(uint8_t *dst, const uint8_t *src, int64_t bytes, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(blocks), dim3(256), 0, s, dst, src, bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_hbm_read(const uint8_t *src, int64_t bytes, float *sink, hipStream_t s) {
+  const int64_t n16 = bytes >> 4;
+  int blocks = (int)std::min<int64_t>(256 * 16, (n16 + 255) / 256);
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const u32x4 *>(src), n16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace oes

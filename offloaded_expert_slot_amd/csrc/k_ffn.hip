@@ -1,0 +1,449 @@
+// Decode expert FFN on the slot cache: grouped GEMVs with dequantisation in registers.
+//
+// FreeToken architecture walk-through §5 (hits are computed straight from the slot
+// cache) and §6 (the FP8 block linear and NVFP4 fused MoE kernels this replaces).
+// For every token t and routed pair j (slot s = slot_ids[t, j], weight w[t, j]):
+//   h_tj = silu(Wg[s] . x_t) * (Wu[s] . x_t)          (gate_up_act kernel)
+//   y_t  = sum_j w[t, j] * (Wd[s] . h_tj)               (down_combine kernel)
+//
+// Both kernels are HBM-bound GEMVs.  A weight row is read as 16-byte chunks;
+// a subgroup of G lanes (G | 64) owns one row at a time, lane l taking chunks
+// l, l + G, l + 2G, ... so each 16-byte load instruction of a wave covers 64
+// consecutive chunks of one or more rows (fully coalesced).  All chunk loads
+// of a row (and of its partner row) are issued before any arithmetic.
+// Weights are turned into bf16 pairs in registers - exactly, since e4m3 and
+// e2m1 values are bf16 numbers - and multiplied with bf16 operands held in LDS
+// by v_dot2_f32_bf16 (fp32 accumulation).  Per-block scales (fp8: one fp32 per
+// 128x128 block; nvfp4: one e4m3 per 16 elements) multiply the partial sums;
+// the nvfp4 per-row fp16 global multiplies the finished row sum.  Lane sums are
+// reduced with cross-lane shuffles.  h is kept as bf16 between the kernels.
+// y is bf16, rounded to nearest even.
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "oes_internal.h"
+
+namespace oes {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kMaxQ = 8;   // chunks per lane per pass
+constexpr int kItemBatch = 2;
+
+// ------------------------------------------------------------------ element decoders
+__device__ inline float dot2(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), acc,
+                                         false);
+}
+// two e4m3 bytes (bytes 0,1 or 2,3 of w) -> packed bf16 pair (exact)
+template <bool HI>
+__device__ inline uint32_t fp8_pair_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ inline f32x2 fp8_pair_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+// the two e2m1 codes of byte B of w (low nibble first) -> packed bf16 pair (exact)
+template <int B>
+__device__ inline uint32_t fp4_pair_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+}
+__device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline float fp16_to_f32(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
+
+// ------------------------------------------------------------------ matrix views
+// One matrix (gate_up or down) of the slot banks, for every slot.
+struct Mat {
+  const uint8_t *codes;   // slot s, row r at codes + s*codes_slot + r*row_bytes
+  int64_t codes_slot, row_bytes;
+  const uint8_t *scale;   // fp8: f32 [rows/128][K/128]; nvfp4: e4m3 [rows][K/16]
+  int64_t scale_slot;
+  int32_t scale_ld;
+  const uint8_t *glob;    // nvfp4: fp16 [rows]
+  int64_t glob_slot;
+  int32_t rows, K, C;     // C = chunks per row
+};
+
+// Registers of one row's chunks (this lane's share).
+struct RowRegs {
+  u32x4 w[kMaxQ];
+  uint32_t sc[kMaxQ];
+};
+
+template <int FMT, int G>
+__device__ inline void load_row(RowRegs &R, const Mat &m, int slot, int row, int lg, int q0, int nq) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(m.codes + (int64_t)slot * m.codes_slot + (int64_t)row * m.row_bytes);
+#pragma unroll
+  for (int q = 0; q < kMaxQ; ++q) {
+    if (q < nq) {
+      const int c = (q0 + q) * G + lg;
+      R.w[q] = __builtin_nontemporal_load(p + c);
+      if (FMT == OES_FP8_BLOCK128) {
+        const float *s = reinterpret_cast<const float *>(m.scale + (int64_t)slot * m.scale_slot);
+        R.sc[q] = __float_as_uint(s[(row >> 7) * m.scale_ld + (c >> 3)]);
+      } else if (FMT == OES_NVFP4) {
+        const uint16_t *s = reinterpret_cast<const uint16_t *>(m.scale + (int64_t)slot * m.scale_slot +
+                                                               (int64_t)row * m.scale_ld);
+        R.sc[q] = s[c];
+      }
+    }
+  }
+}
+
+// Partial dot product of this lane's chunks of a row with a bf16 operand vector in LDS.
+template <int FMT, int G>
+__device__ inline float dot_row(const RowRegs &R, const uint16_t *op, int lg, int q0, int nq) {
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxQ; ++q) {
+    if (q < nq) {
+      const int c = (q0 + q) * G + lg;
+      const u32x4 w = R.w[q];
+      if (FMT == OES_BF16) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(op + c * 8);
+        acc = dot2(w.x, x.x, acc);
+        acc = dot2(w.y, x.y, acc);
+        acc = dot2(w.z, x.z, acc);
+        acc = dot2(w.w, x.w, acc);
+      } else if (FMT == OES_FP8_BLOCK128) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(op + c * 16);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(op + c * 16 + 8);
+        float s = 0.f;
+        s = dot2(fp8_pair_bf16<false>(w.x), x0.x, s);
+        s = dot2(fp8_pair_bf16<true>(w.x), x0.y, s);
+        s = dot2(fp8_pair_bf16<false>(w.y), x0.z, s);
+        s = dot2(fp8_pair_bf16<true>(w.y), x0.w, s);
+        s = dot2(fp8_pair_bf16<false>(w.z), x1.x, s);
+        s = dot2(fp8_pair_bf16<true>(w.z), x1.y, s);
+        s = dot2(fp8_pair_bf16<false>(w.w), x1.z, s);
+        s = dot2(fp8_pair_bf16<true>(w.w), x1.w, s);
+        acc = fmaf(s, __uint_as_float(R.sc[q]), acc);
+      } else {  // NVFP4: 32 elements, two 16-element scale blocks
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(op + c * 32);
+        const u32x4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+        float s0 = 0.f, s1 = 0.f;
+        s0 = dot2(fp4_pair_bf16<0>(w.x), x0.x, s0);
+        s0 = dot2(fp4_pair_bf16<1>(w.x), x0.y, s0);
+        s0 = dot2(fp4_pair_bf16<2>(w.x), x0.z, s0);
+        s0 = dot2(fp4_pair_bf16<3>(w.x), x0.w, s0);
+        s0 = dot2(fp4_pair_bf16<0>(w.y), x1.x, s0);
+        s0 = dot2(fp4_pair_bf16<1>(w.y), x1.y, s0);
+        s0 = dot2(fp4_pair_bf16<2>(w.y), x1.z, s0);
+        s0 = dot2(fp4_pair_bf16<3>(w.y), x1.w, s0);
+        s1 = dot2(fp4_pair_bf16<0>(w.z), x2.x, s1);
+        s1 = dot2(fp4_pair_bf16<1>(w.z), x2.y, s1);
+        s1 = dot2(fp4_pair_bf16<2>(w.z), x2.z, s1);
+        s1 = dot2(fp4_pair_bf16<3>(w.z), x2.w, s1);
+        s1 = dot2(fp4_pair_bf16<0>(w.w), x3.x, s1);
+        s1 = dot2(fp4_pair_bf16<1>(w.w), x3.y, s1);
+        s1 = dot2(fp4_pair_bf16<2>(w.w), x3.z, s1);
+        s1 = dot2(fp4_pair_bf16<3>(w.w), x3.w, s1);
+        const f32x2 sc = fp8_pair_f32<false>(R.sc[q]);
+        acc = fmaf(s0, sc.x, acc);
+        acc = fmaf(s1, sc.y, acc);
+      }
+    }
+  }
+  return acc;
+}
+
+template <int G>
+__device__ inline float group_sum(float v) {
+#pragma unroll
+  for (int d = G / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, G);
+  return v;
+}
+
+template <int FMT>
+__device__ inline float row_global(const Mat &m, int slot, int row) {
+  if (FMT == OES_NVFP4) {
+    const uint16_t *g = reinterpret_cast<const uint16_t *>(m.glob + (int64_t)slot * m.glob_slot);
+    return fp16_to_f32(g[row]);
+  }
+  return 1.f;
+}
+
+struct KArgs {
+  FfnArgs f;
+  Mat gu, dn;
+};
+
+// Copies `count` bf16 values (count % 8 == 0) from global to LDS.
+__device__ inline void stage_bf16(uint16_t *dst, const uint16_t *src, int count) {
+  const u32x4 *s = reinterpret_cast<const u32x4 *>(src);
+  u32x4 *d = reinterpret_cast<u32x4 *>(dst);
+  for (int i = threadIdx.x; i < count / 8; i += kThreads) d[i] = s[i];
+}
+
+// ------------------------------------------------------------------ gate_up + act
+// grid: (ceil(I / NSG), n*k); each subgroup owns one (gate row, up row) pair.
+template <int FMT, int G>
+__global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
+  extern __shared__ __align__(16) uint16_t xs[];
+  const FfnArgs &a = ka.f;
+  if (a.gate && *a.gate == 0) return;
+  const int p = blockIdx.y;
+  const int slot = a.slot_ids[p];
+  if (slot < 0) return;
+  if (slot >= a.S) {
+    if (threadIdx.x == 0) atomicCAS(a.err, 0, (int)OES_ERR_ARG);
+    return;
+  }
+  const int t = p / a.k;
+  stage_bf16(xs, a.x + (int64_t)t * a.H, a.H);
+  __syncthreads();
+  constexpr int NSG = kThreads / G;
+  const int sg = threadIdx.x / G, lg = threadIdx.x % G;
+  const int r = blockIdx.x * NSG + sg;
+  if (r >= a.I) return;
+  const Mat &m = ka.gu;
+  float g = 0.f, u = 0.f;
+  for (int q0 = 0; q0 * G < m.C; q0 += kMaxQ) {
+    const int nq = min(kMaxQ, m.C / G - q0);
+    RowRegs Rg, Ru;
+    load_row<FMT, G>(Rg, m, slot, r, lg, q0, nq);
+    load_row<FMT, G>(Ru, m, slot, a.I + r, lg, q0, nq);
+    g += dot_row<FMT, G>(Rg, xs, lg, q0, nq);
+    u += dot_row<FMT, G>(Ru, xs, lg, q0, nq);
+  }
+  g = group_sum<G>(g);
+  u = group_sum<G>(u);
+  if (lg == 0) {
+    g *= row_global<FMT>(m, slot, r);
+    u *= row_global<FMT>(m, slot, a.I + r);
+    const float hv = g / (1.f + __expf(-g)) * u;
+    reinterpret_cast<uint16_t *>(a.h)[(int64_t)p * a.I + r] = f32_to_bf16_rne(hv);
+  }
+}
+
+// ------------------------------------------------------------------ down + combine
+// grid: (ceil(H / RB), n); work items = RB rows x k pairs, reduced per row in pair order.
+template <int FMT, int G>
+__global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int RB) {
+  extern __shared__ __align__(16) uint16_t hs[];  // [k][I] bf16, then red[RB*k] floats
+  const FfnArgs &a = ka.f;
+  if (a.gate && *a.gate == 0) return;
+  __shared__ int sl[32];
+  __shared__ float wt[32];
+  const int t = blockIdx.y;
+  const int k = a.k, I = a.I;
+  float *red = reinterpret_cast<float *>(hs + (int64_t)k * I);
+  if (threadIdx.x < k) {
+    int s = a.slot_ids[(int64_t)t * k + threadIdx.x];
+    if (s >= a.S) {
+      atomicCAS(a.err, 0, (int)OES_ERR_ARG);
+      s = -1;
+    }
+    sl[threadIdx.x] = s;
+    wt[threadIdx.x] = a.w[(int64_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const uint16_t *hsrc = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)t * k * I;
+  for (int j = 0; j < k; ++j)
+    if (sl[j] >= 0) stage_bf16(hs + (int64_t)j * I, hsrc + (int64_t)j * I, I);
+  __syncthreads();
+  constexpr int NSG = kThreads / G;
+  const int sg = threadIdx.x / G, lg = threadIdx.x % G;
+  const int r0 = blockIdx.x * RB;
+  const int items = RB * k;
+  const Mat &m = ka.dn;
+  const int nqt = m.C / G;
+  for (int it0 = sg * kItemBatch; it0 < items; it0 += NSG * kItemBatch) {
+    float acc[kItemBatch];
+    int rows[kItemBatch], js[kItemBatch], slots[kItemBatch];
+#pragma unroll
+    for (int b = 0; b < kItemBatch; ++b) {
+      const int it = it0 + b;
+      acc[b] = 0.f;
+      rows[b] = r0 + it / k;
+      js[b] = it % k;
+      slots[b] = (it < items && rows[b] < a.H) ? sl[js[b]] : -1;
+    }
+    for (int q0 = 0; q0 < nqt; q0 += kMaxQ) {
+      const int nq = min(kMaxQ, nqt - q0);
+      RowRegs R[kItemBatch];
+#pragma unroll
+      for (int b = 0; b < kItemBatch; ++b)
+        if (slots[b] >= 0) load_row<FMT, G>(R[b], m, slots[b], rows[b], lg, q0, nq);
+#pragma unroll
+      for (int b = 0; b < kItemBatch; ++b)
+        if (slots[b] >= 0) acc[b] += dot_row<FMT, G>(R[b], hs + (int64_t)js[b] * I, lg, q0, nq);
+    }
+#pragma unroll
+    for (int b = 0; b < kItemBatch; ++b) {
+      const float v = group_sum<G>(acc[b]);
+      const int it = it0 + b;
+      if (lg == 0 && it < items) red[it] = slots[b] >= 0 ? v * row_global<FMT>(m, slots[b], rows[b]) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < RB) {
+    const int row = r0 + threadIdx.x;
+    if (row < a.H) {
+      float s = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (sl[j] >= 0) s = fmaf(wt[j], red[threadIdx.x * k + j], s);
+      a.y[(int64_t)t * a.H + row] = f32_to_bf16_rne(s);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+int pick_group(int C) {
+  if (C % 64 == 0) return 64;
+  if (C % 32 == 0) return 32;
+  if (C % 16 == 0) return 16;
+  if (C % 8 == 0) return 8;
+  return 0;
+}
+
+int epc_of(int fmt) {
+  return fmt == OES_BF16 ? 8 : fmt == OES_FP8_BLOCK128 ? 16 : fmt == OES_NVFP4 ? 32 : 0;
+}
+
+Mat make_mat(const FfnArgs &a, bool down) {
+  Mat m = {};
+  const int fmt = a.format;
+  const int rows = down ? a.H : 2 * a.I;
+  const int K = down ? a.I : a.H;
+  m.rows = rows;
+  m.K = K;
+  m.C = K / epc_of(fmt);
+  int bc = 0, bs = -1, bg = -1;
+  if (fmt == OES_BF16) {
+    bc = down ? 1 : 0;
+  } else if (fmt == OES_FP8_BLOCK128) {
+    bc = down ? 2 : 0;
+    bs = bc + 1;
+  } else {
+    bc = down ? 3 : 0;
+    bs = bc + 1;
+    bg = bc + 2;
+  }
+  m.codes = a.bank[bc];
+  m.codes_slot = a.row_bytes[bc];
+  m.row_bytes = m.codes_slot / rows;
+  if (bs >= 0) {
+    m.scale = a.bank[bs];
+    m.scale_slot = a.row_bytes[bs];
+    m.scale_ld = fmt == OES_FP8_BLOCK128 ? K / 128 : K / 16;
+  }
+  if (bg >= 0) {
+    m.glob = a.bank[bg];
+    m.glob_slot = a.row_bytes[bg];
+  }
+  return m;
+}
+
+template <int FMT, int G>
+hipError_t launch_gate_up_g(const KArgs &ka, hipStream_t s) {
+  const FfnArgs &a = ka.f;
+  constexpr int NSG = kThreads / G;
+  dim3 grid((a.I + NSG - 1) / NSG, a.n * a.k);
+  hipLaunchKernelGGL((gate_up_kernel<FMT, G>), grid, dim3(kThreads), (size_t)a.H * 2, s, ka);
+  return hipGetLastError();
+}
+
+template <int FMT, int G>
+hipError_t launch_down_g(const KArgs &ka, hipStream_t s) {
+  const FfnArgs &a = ka.f;
+  int rb = (int)std::min<int64_t>(16, std::max<int64_t>(1, (int64_t)a.H * a.n / 1024));
+  while (rb & (rb - 1)) rb &= rb - 1;  // power of two
+  dim3 grid((a.H + rb - 1) / rb, a.n);
+  const size_t lds = (size_t)a.k * a.I * 2 + (size_t)rb * a.k * 4;
+  hipLaunchKernelGGL((down_kernel<FMT, G>), grid, dim3(kThreads), lds, s, ka, rb);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const KArgs &ka, hipStream_t s) {
+  hipError_t e;
+  switch (pick_group(ka.gu.C)) {
+    case 64: e = launch_gate_up_g<FMT, 64>(ka, s); break;
+    case 32: e = launch_gate_up_g<FMT, 32>(ka, s); break;
+    case 16: e = launch_gate_up_g<FMT, 16>(ka, s); break;
+    case 8: e = launch_gate_up_g<FMT, 8>(ka, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  switch (pick_group(ka.dn.C)) {
+    case 64: return launch_down_g<FMT, 64>(ka, s);
+    case 32: return launch_down_g<FMT, 32>(ka, s);
+    case 16: return launch_down_g<FMT, 16>(ka, s);
+    case 8: return launch_down_g<FMT, 8>(ka, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------------ decoder check
+__global__ void debug_decode_kernel(int elem, const uint8_t *codes, int n, float *out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (elem == OES_ELEM_FP4X2) {
+    // i indexes a byte: elements 2i and 2i+1
+    if (2 * i >= n) return;
+    const uint32_t word = codes[i];
+    const uint32_t pr = fp4_pair_bf16<0>(word);
+    out[2 * i] = bf16_to_f32(pr & 0xffffu);
+    if (2 * i + 1 < n) out[2 * i + 1] = bf16_to_f32(pr >> 16);
+    return;
+  }
+  if (i >= n) return;
+  if (elem == OES_ELEM_E4M3) {
+    out[i] = fp8_pair_f32<false>((uint32_t)codes[i]).x;
+  } else if (elem == OES_ELEM_E8M0) {
+    const uint32_t e = codes[i];
+    out[i] = e == 255 ? __uint_as_float(0x7fc00000u) : (e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23));
+  } else if (elem == OES_ELEM_BF16) {
+    out[i] = bf16_to_f32(reinterpret_cast<const uint16_t *>(codes)[i]);
+  } else if (elem == OES_ELEM_FP16) {
+    out[i] = fp16_to_f32(reinterpret_cast<const uint16_t *>(codes)[i]);
+  }
+}
+
+}  // namespace
+
+bool expert_ffn_supported(int format, int H, int I, int k) {
+  const int epc = epc_of(format);
+  if (!epc) return false;
+  if (H % epc || I % epc) return false;
+  if (!pick_group(H / epc) || !pick_group(I / epc)) return false;
+  if (H > 16384) return false;                       // x row in LDS
+  if ((int64_t)k * I * 2 + 16 * k * 4 > 65536) return false;  // h rows of a token in LDS
+  return true;
+}
+
+hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t s) {
+  KArgs ka;
+  ka.f = a;
+  ka.gu = make_mat(a, false);
+  ka.dn = make_mat(a, true);
+  switch (a.format) {
+    case OES_BF16: return launch_fmt<OES_BF16>(ka, s);
+    case OES_FP8_BLOCK128: return launch_fmt<OES_FP8_BLOCK128>(ka, s);
+    case OES_NVFP4: return launch_fmt<OES_NVFP4>(ka, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_debug_decode(int elem, const uint8_t *codes, int n, float *out, hipStream_t s) {
+  const int items = elem == OES_ELEM_FP4X2 ? (n + 1) / 2 : n;
+  hipLaunchKernelGGL(debug_decode_kernel, dim3((items + 255) / 256), dim3(256), 0, s, elem, codes, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace oes

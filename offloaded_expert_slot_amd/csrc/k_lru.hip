@@ -1,0 +1,221 @@
+// ensure_experts on the device: the global LRU remap of one layer's routed experts
+// onto the slot pool, done by a single 1024-thread workgroup out of LDS.
+//
+// FreeToken MoE benchmark guide §4.1 and §4.3, FreeToken architecture walk-through
+// §5: experts are named by the flat id layer * E + expert; one slot pool serves
+// every layer; a step remaps its routed experts with a global LRU policy and the
+// missing ones are then copied in.
+//
+// Batch rules (the pages give the policy, not the batch order):
+//   U    = sorted distinct flat ids of the step
+//   hits = members of U already owning a slot; misses = the rest, ascending
+//   victims: slots not holding a member of U, ordered by the key
+//            (not empty, stamp, owner, slot) - the i-th miss takes the i-th
+//   |U| > S fails with OES_ERR_CAPACITY and writes nothing to the table
+//   on success clock += 1 and every slot holding a member of U gets the clock.
+//
+// Layout in LDS (E <= 4096, S <= 4096):
+//   req[E]   u8   expert e of this layer requested
+//   emap[E]  i32  slot owning expert e of this layer, or -1
+//   mrank[E] i32  rank of expert e among the misses (exclusive scan)
+//   khi/klo[Spad] u64  victim keys, bitonic-sorted ascending; members of U and
+//                      padding get the all-ones key and sort last.
+// Key encoding: khi = (owner != -1) << 63 | stamp  (stamps < 2^62),
+//               klo = (owner + 1) << 12 | slot     (owner < 2^50, slot < 4096).
+
+#include "oes_internal.h"
+
+namespace oes {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kPerThread = OES_MAX_EXPERTS / kThreads;  // 4 experts per thread in the scan
+constexpr uint64_t kMax = ~0ull;
+
+// Block-wide exclusive scan of one int per thread; returns the exclusive prefix, *total the sum.
+__device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      int t = wave_tot[w];
+      wave_tot[w] = run;
+      run += t;
+    }
+    wave_tot[kWaves] = run;
+  }
+  __syncthreads();
+  int excl = wave_tot[wave] + inc - v;
+  *total = wave_tot[kWaves];
+  __syncthreads();
+  return excl;
+}
+
+__device__ inline bool key_less(uint64_t ah, uint64_t al, uint64_t bh, uint64_t bl) {
+  return ah < bh || (ah == bh && al < bl);
+}
+
+__global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
+  __shared__ uint64_t khi[OES_MAX_SLOTS];
+  __shared__ uint64_t klo[OES_MAX_SLOTS];
+  __shared__ int32_t emap[OES_MAX_EXPERTS];
+  __shared__ int32_t mrank[OES_MAX_EXPERTS];
+  __shared__ uint8_t req[OES_MAX_EXPERTS];
+  __shared__ int wave_tot[kWaves + 1];
+  __shared__ int s_bad, s_evict;
+  __shared__ uint64_t s_clock;
+
+  const int tid = threadIdx.x;
+  const int E = a.E, S = a.S;
+  const int64_t base = (int64_t)a.layer * E;
+
+  for (int e = tid; e < E; e += kThreads) {
+    req[e] = 0;
+    emap[e] = -1;
+  }
+  if (tid == 0) {
+    s_bad = 0;
+    s_evict = 0;
+    s_clock = a.ctl->clock;
+  }
+  __syncthreads();
+
+  // 1. mark requested experts, validate ids
+  for (int i = tid; i < a.nk; i += kThreads) {
+    const int id = a.ids[i];
+    if (id < 0 || id >= E)
+      s_bad = 1;
+    else
+      req[id] = 1;
+  }
+  // 2. experts of this layer that already own a slot
+  for (int s = tid; s < S; s += kThreads) {
+    const int64_t o = a.owner[s];
+    if (o >= base && o < base + E) emap[(int)(o - base)] = s;
+  }
+  __syncthreads();
+
+  // 3. misses: requested experts without a slot, ranked in ascending expert order
+  int cnt_req = 0, cnt_miss = 0;
+  const int e0 = tid * kPerThread;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int e = e0 + q;
+    if (e < E && req[e]) {
+      ++cnt_req;
+      if (emap[e] < 0) ++cnt_miss;
+    }
+  }
+  int nU = 0, nM = 0;
+  (void)block_exclusive_scan(cnt_req, wave_tot, &nU);
+  int mbase = block_exclusive_scan(cnt_miss, wave_tot, &nM);
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int e = e0 + q;
+    if (e < E) {
+      const bool m = req[e] && emap[e] < 0;
+      mrank[e] = m ? mbase : -1;
+      if (m) ++mbase;
+    }
+  }
+
+  const bool bad = s_bad != 0;
+  const bool over = nU > S;
+  if (bad || over) {
+    for (int i = tid; i < a.nk; i += kThreads) a.slot_ids[i] = -1;
+    if (tid == 0) {
+      if (a.ctl->err == OES_OK) a.ctl->err = bad ? OES_ERR_ARG : OES_ERR_CAPACITY;
+      a.ctl->step_ok = 0;
+      a.ctl->miss_count = 0;
+      a.ctl->failed_steps += 1;
+    }
+    return;
+  }
+
+  if (nM > 0) {
+    // 4. victim keys; slots holding a member of U are not evictable
+    for (int s = tid; s < a.Spad; s += kThreads) {
+      uint64_t hi = kMax, lo = kMax;
+      if (s < S) {
+        const int64_t o = a.owner[s];
+        const bool in_u = o >= base && o < base + E && req[(int)(o - base)];
+        if (!in_u) {
+          hi = ((o != -1) ? (1ull << 63) : 0ull) | a.stamp[s];
+          lo = ((uint64_t)(o + 1) << 12) | (uint64_t)s;
+        }
+      }
+      khi[s] = hi;
+      klo[s] = lo;
+    }
+    __syncthreads();
+    // 5. bitonic sort ascending
+    const int half = a.Spad >> 1;
+    for (int kk = 2; kk <= a.Spad; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < half; i += kThreads) {
+          const int lo_i = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+          const int hi_i = lo_i | j;
+          const bool asc = (lo_i & kk) == 0;
+          const uint64_t ah = khi[lo_i], al = klo[lo_i], bh = khi[hi_i], bl = klo[hi_i];
+          const bool gt = key_less(bh, bl, ah, al);
+          if (gt == asc) {
+            khi[lo_i] = bh; klo[lo_i] = bl;
+            khi[hi_i] = ah; klo[hi_i] = al;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // 6. install: the i-th miss takes the i-th victim
+    for (int e = tid; e < E; e += kThreads) {
+      const int r = mrank[e];
+      if (r >= 0) {
+        const int v = (int)(klo[r] & 0xFFFull);
+        const int64_t old = a.owner[v];
+        if (old != -1) atomicAdd(&s_evict, 1);
+        a.owner[v] = base + e;
+        emap[e] = v;
+        a.miss_slot[r] = v;
+        a.miss_id[r] = base + e;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 7. stamp every slot holding a member of U, then the slot map
+  const uint64_t T = s_clock + 1;
+  for (int e = tid; e < E; e += kThreads)
+    if (req[e]) a.stamp[emap[e]] = T;
+  for (int i = tid; i < a.nk; i += kThreads) a.slot_ids[i] = emap[a.ids[i]];
+  if (tid == 0) {
+    Ctl *c = a.ctl;
+    c->clock = T;
+    c->step_ok = 1;
+    c->miss_count = nM;
+    c->steps += 1;
+    c->hits += (uint64_t)(nU - nM);
+    c->misses += (uint64_t)nM;
+    c->evictions += (uint64_t)s_evict;
+    c->bytes += (uint64_t)nM * (uint64_t)a.bpe;
+    c->last_misses = (uint32_t)nM;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lru_remap(const LruArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(lru_remap_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace oes
