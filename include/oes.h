@@ -149,6 +149,16 @@ oes_status oes_cache_set_source(oes_cache *c, int32_t bank, int32_t layer, const
  * clock < 2^62.  Enqueued on `stream` (host arrays are copied before return). */
 oes_status oes_cache_set_state(oes_cache *c, const int64_t *owner, const uint64_t *stamp,
                                uint64_t clock, void *stream);
+/* Device-side snapshot of the slot table (owners, stamps, clock): snapshot
+ * copies the live table into a cache-owned device buffer, restore copies it
+ * back and clears the miss list and the step status (the sticky error is
+ * kept).  Device-to-device copies enqueued on `stream`, no host sync: lets a
+ * caller re-run a step from the same state many times back to back (the copy
+ * benchmark's repeats, benchmark guide §4.3).  restore before any snapshot
+ * returns OES_ERR_STATE. */
+oes_status oes_cache_snapshot(oes_cache *c, void *stream);
+oes_status oes_cache_restore(oes_cache *c, void *stream);
+
 /* Read the slot table into host arrays of num_slots entries (any pointer may
  * be NULL).  Syncs `stream`. */
 oes_status oes_cache_get_state(oes_cache *c, int64_t *owner, uint64_t *stamp, uint64_t *clock,

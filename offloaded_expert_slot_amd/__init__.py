@@ -82,6 +82,8 @@ _SIGS = {
     "oes_cache_set_source": (_I32, [_P, _I32, _I32, _P, _I64]),
     "oes_cache_set_state": (_I32, [_P, _PI64, _PU64, _U64, _P]),
     "oes_cache_get_state": (_I32, [_P, _PI64, _PU64, _PU64, _P]),
+    "oes_cache_snapshot": (_I32, [_P, _P]),
+    "oes_cache_restore": (_I32, [_P, _P]),
     "oes_cache_load_rows": (_I32, [_P, _PI32, _PI64, _I32, _P]),
     "oes_cache_fill_slots": (_I32, [_P, _U8, _P]),
     "oes_cache_slot_bank": (_I32, [_P, _I32, ctypes.POINTER(_P), _PI64]),
@@ -227,6 +229,12 @@ class Cache:
         _check(lib().oes_cache_get_state(self._h, owner.ctypes.data_as(_PI64), stamp.ctypes.data_as(_PU64),
                                          ctypes.byref(clock), _stream(stream)))
         return owner, stamp, int(clock.value)
+
+    def snapshot(self, stream=None):
+        _check(lib().oes_cache_snapshot(self._h, _stream(stream)))
+
+    def restore(self, stream=None):
+        _check(lib().oes_cache_restore(self._h, _stream(stream)))
 
     def load_rows(self, slots, ids, stream=None):
         slots = np.ascontiguousarray(slots, dtype=np.int32)

@@ -171,6 +171,8 @@ struct oes_cache {
   int64_t staging_bytes = 0;
   hipEvent_t staging_done = nullptr;
   int fused_copy = 1, copy_mode = OES_COPY_ZERO, copy_blocks = 0;
+  uint8_t *snap = nullptr;  // device snapshot: owner | stamp | clock
+  bool has_snap = false;
 };
 
 struct oes_layers {
@@ -268,6 +270,7 @@ static void cache_free(oes_cache *c) {
   for (int b = 0; b < OES_MAX_BANKS; ++b)
     if (c->slot_bank[b]) (void)hipFree(c->slot_bank[b]);
   if (c->dblock) (void)hipFree(c->dblock);
+  if (c->snap) (void)hipFree(c->snap);
   if (c->staging) (void)hipHostFree(c->staging);
   if (c->staging_done) (void)hipEventDestroy(c->staging_done);
   c->src.release();
@@ -450,6 +453,39 @@ extern "C" oes_status oes_cache_set_state(oes_cache *c, const int64_t *owner, co
   static_assert(offsetof(Ctl, clock) == 0 && offsetof(Ctl, miss_count) == 16, "Ctl layout");
   HIP_TRY(hipMemcpyAsync(c->ctl, hc, 20, hipMemcpyHostToDevice, s));
   HIP_TRY(hipEventRecord(c->staging_done, s));
+  return OES_OK;
+}
+
+extern "C" oes_status oes_cache_snapshot(oes_cache *c, void *stream) {
+  if (!c) return fail(OES_ERR_ARG, "cache is NULL");
+  DeviceGuard g(c->device);
+  const size_t S = (size_t)c->S;
+  if (!c->snap) {
+    hipError_t e = hipMalloc(&c->snap, 16 * S + 64);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(OES_ERR_NOMEM, "hipMalloc of the snapshot failed");
+    }
+  }
+  hipStream_t s = as_stream(stream);
+  HIP_TRY(hipMemcpyAsync(c->snap, c->owner, 8 * S, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(c->snap + 8 * S, c->stamp, 8 * S, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(c->snap + 16 * S, &c->ctl->clock, 8, hipMemcpyDeviceToDevice, s));
+  c->has_snap = true;
+  return OES_OK;
+}
+
+extern "C" oes_status oes_cache_restore(oes_cache *c, void *stream) {
+  if (!c) return fail(OES_ERR_ARG, "cache is NULL");
+  if (!c->has_snap) return fail(OES_ERR_STATE, "no snapshot taken");
+  DeviceGuard g(c->device);
+  const size_t S = (size_t)c->S;
+  hipStream_t s = as_stream(stream);
+  HIP_TRY(hipMemcpyAsync(c->owner, c->snap, 8 * S, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(c->stamp, c->snap + 8 * S, 8 * S, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(&c->ctl->clock, c->snap + 16 * S, 8, hipMemcpyDeviceToDevice, s));
+  launch_reset_step(c->ctl, s);
+  HIP_TRY(hipGetLastError());
   return OES_OK;
 }
 
@@ -878,6 +914,8 @@ extern "C" oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x
                                      void *compute_stream) {
   if (!p) return fail(OES_ERR_ARG, "layers is NULL");
   if (p->sc.format != OES_MXFP4_T) return fail(OES_ERR_UNSUPPORTED, "layer FFN is implemented for OES_MXFP4_T");
+  if (!prefill_supported(p->sc.hidden, p->sc.inter, p->sc.num_experts))
+    return fail(OES_ERR_UNSUPPORTED, "layer FFN needs H and I multiples of 64");
   if (layer < 0 || layer >= p->sc.num_layers) return fail(OES_ERR_ARG, "layer out of range");
   const int d = layer % p->depth;
   if (p->resident[d] != layer) return fail(OES_ERR_STATE, "layer %d was not prefetched", layer);

@@ -36,7 +36,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kMaxQ = 8;   // chunks per lane per pass
-constexpr int kItemBatch = 2;
 
 // ------------------------------------------------------------------ element decoders
 __device__ inline float dot2(uint32_t w, uint32_t x, float acc) {
@@ -105,58 +104,74 @@ __device__ inline void load_row(RowRegs &R, const Mat &m, int slot, int row, int
   }
 }
 
+// Dot product of one 16-byte weight chunk (EPC elements) with its bf16 operand
+// (EPC/8 16-byte vectors at xo, in LDS or registers); fp8 / nvfp4 block scales
+// (packed in sc) are applied here.
+template <int FMT>
+__device__ inline float dot_chunk(const u32x4 w, uint32_t sc, const u32x4 *xo) {
+  if (FMT == OES_BF16) {
+    const u32x4 x = xo[0];
+    float acc = 0.f;
+    acc = dot2(w.x, x.x, acc);
+    acc = dot2(w.y, x.y, acc);
+    acc = dot2(w.z, x.z, acc);
+    acc = dot2(w.w, x.w, acc);
+    return acc;
+  } else if (FMT == OES_FP8_BLOCK128) {
+    const u32x4 x0 = xo[0], x1 = xo[1];
+    float s = 0.f;
+    s = dot2(fp8_pair_bf16<false>(w.x), x0.x, s);
+    s = dot2(fp8_pair_bf16<true>(w.x), x0.y, s);
+    s = dot2(fp8_pair_bf16<false>(w.y), x0.z, s);
+    s = dot2(fp8_pair_bf16<true>(w.y), x0.w, s);
+    s = dot2(fp8_pair_bf16<false>(w.z), x1.x, s);
+    s = dot2(fp8_pair_bf16<true>(w.z), x1.y, s);
+    s = dot2(fp8_pair_bf16<false>(w.w), x1.z, s);
+    s = dot2(fp8_pair_bf16<true>(w.w), x1.w, s);
+    return s * __uint_as_float(sc);
+  } else {  // NVFP4: 32 elements, two 16-element scale blocks
+    const u32x4 x0 = xo[0], x1 = xo[1], x2 = xo[2], x3 = xo[3];
+    float s0 = 0.f, s1 = 0.f;
+    s0 = dot2(fp4_pair_bf16<0>(w.x), x0.x, s0);
+    s0 = dot2(fp4_pair_bf16<1>(w.x), x0.y, s0);
+    s0 = dot2(fp4_pair_bf16<2>(w.x), x0.z, s0);
+    s0 = dot2(fp4_pair_bf16<3>(w.x), x0.w, s0);
+    s0 = dot2(fp4_pair_bf16<0>(w.y), x1.x, s0);
+    s0 = dot2(fp4_pair_bf16<1>(w.y), x1.y, s0);
+    s0 = dot2(fp4_pair_bf16<2>(w.y), x1.z, s0);
+    s0 = dot2(fp4_pair_bf16<3>(w.y), x1.w, s0);
+    s1 = dot2(fp4_pair_bf16<0>(w.z), x2.x, s1);
+    s1 = dot2(fp4_pair_bf16<1>(w.z), x2.y, s1);
+    s1 = dot2(fp4_pair_bf16<2>(w.z), x2.z, s1);
+    s1 = dot2(fp4_pair_bf16<3>(w.z), x2.w, s1);
+    s1 = dot2(fp4_pair_bf16<0>(w.w), x3.x, s1);
+    s1 = dot2(fp4_pair_bf16<1>(w.w), x3.y, s1);
+    s1 = dot2(fp4_pair_bf16<2>(w.w), x3.z, s1);
+    s1 = dot2(fp4_pair_bf16<3>(w.w), x3.w, s1);
+    const f32x2 scf = fp8_pair_f32<false>(sc);
+    return fmaf(s0, scf.x, s1 * scf.y);
+  }
+}
+
+template <int FMT>
+struct Epc;
+template <>
+struct Epc<OES_BF16> { static constexpr int v = 8; };
+template <>
+struct Epc<OES_FP8_BLOCK128> { static constexpr int v = 16; };
+template <>
+struct Epc<OES_NVFP4> { static constexpr int v = 32; };
+
 // Partial dot product of this lane's chunks of a row with a bf16 operand vector in LDS.
 template <int FMT, int G>
 __device__ inline float dot_row(const RowRegs &R, const uint16_t *op, int lg, int q0, int nq) {
+  constexpr int EPC = Epc<FMT>::v;
   float acc = 0.f;
 #pragma unroll
   for (int q = 0; q < kMaxQ; ++q) {
     if (q < nq) {
       const int c = (q0 + q) * G + lg;
-      const u32x4 w = R.w[q];
-      if (FMT == OES_BF16) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(op + c * 8);
-        acc = dot2(w.x, x.x, acc);
-        acc = dot2(w.y, x.y, acc);
-        acc = dot2(w.z, x.z, acc);
-        acc = dot2(w.w, x.w, acc);
-      } else if (FMT == OES_FP8_BLOCK128) {
-        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(op + c * 16);
-        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(op + c * 16 + 8);
-        float s = 0.f;
-        s = dot2(fp8_pair_bf16<false>(w.x), x0.x, s);
-        s = dot2(fp8_pair_bf16<true>(w.x), x0.y, s);
-        s = dot2(fp8_pair_bf16<false>(w.y), x0.z, s);
-        s = dot2(fp8_pair_bf16<true>(w.y), x0.w, s);
-        s = dot2(fp8_pair_bf16<false>(w.z), x1.x, s);
-        s = dot2(fp8_pair_bf16<true>(w.z), x1.y, s);
-        s = dot2(fp8_pair_bf16<false>(w.w), x1.z, s);
-        s = dot2(fp8_pair_bf16<true>(w.w), x1.w, s);
-        acc = fmaf(s, __uint_as_float(R.sc[q]), acc);
-      } else {  // NVFP4: 32 elements, two 16-element scale blocks
-        const u32x4 *xp = reinterpret_cast<const u32x4 *>(op + c * 32);
-        const u32x4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
-        float s0 = 0.f, s1 = 0.f;
-        s0 = dot2(fp4_pair_bf16<0>(w.x), x0.x, s0);
-        s0 = dot2(fp4_pair_bf16<1>(w.x), x0.y, s0);
-        s0 = dot2(fp4_pair_bf16<2>(w.x), x0.z, s0);
-        s0 = dot2(fp4_pair_bf16<3>(w.x), x0.w, s0);
-        s0 = dot2(fp4_pair_bf16<0>(w.y), x1.x, s0);
-        s0 = dot2(fp4_pair_bf16<1>(w.y), x1.y, s0);
-        s0 = dot2(fp4_pair_bf16<2>(w.y), x1.z, s0);
-        s0 = dot2(fp4_pair_bf16<3>(w.y), x1.w, s0);
-        s1 = dot2(fp4_pair_bf16<0>(w.z), x2.x, s1);
-        s1 = dot2(fp4_pair_bf16<1>(w.z), x2.y, s1);
-        s1 = dot2(fp4_pair_bf16<2>(w.z), x2.z, s1);
-        s1 = dot2(fp4_pair_bf16<3>(w.z), x2.w, s1);
-        s1 = dot2(fp4_pair_bf16<0>(w.w), x3.x, s1);
-        s1 = dot2(fp4_pair_bf16<1>(w.w), x3.y, s1);
-        s1 = dot2(fp4_pair_bf16<2>(w.w), x3.z, s1);
-        s1 = dot2(fp4_pair_bf16<3>(w.w), x3.w, s1);
-        const f32x2 sc = fp8_pair_f32<false>(R.sc[q]);
-        acc = fmaf(s0, sc.x, acc);
-        acc = fmaf(s1, sc.y, acc);
-      }
+      acc += dot_chunk<FMT>(R.w[q], R.sc[q], reinterpret_cast<const u32x4 *>(op + c * EPC));
     }
   }
   return acc;
@@ -232,17 +247,53 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
 }
 
 // ------------------------------------------------------------------ down + combine
-// grid: (ceil(H / RB), n); work items = RB rows x k pairs, reduced per row in pair order.
-template <int FMT, int G>
+// grid: (ceil(H / RB), n).  Work items are (pair j, row) in pair-major order;
+// subgroup sg takes a contiguous run of items, so it mostly keeps one pair: its
+// share of h_j (NQ chunks of EPC bf16) is loaded once into registers, and rows
+// are processed IB at a time with every weight load issued before the
+// arithmetic.  Per-row results over the pairs are combined in pair order
+// (deterministic) and written as bf16.
+constexpr int kMaxRed = 512;  // RB * k partial results per block (RB <= 16, k <= 32)
+
+template <int NQ>
+struct RowN {
+  u32x4 w[NQ];
+  uint32_t sc[NQ];
+};
+
+template <int FMT, int G, int NQ>
+__device__ inline void load_row_n(RowN<NQ> &R, const Mat &m, int slot, int row, int lg) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(m.codes + (int64_t)slot * m.codes_slot + (int64_t)row * m.row_bytes);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int c = q * G + lg;
+    R.w[q] = __builtin_nontemporal_load(p + c);
+    if (FMT == OES_FP8_BLOCK128) {
+      const float *s = reinterpret_cast<const float *>(m.scale + (int64_t)slot * m.scale_slot);
+      R.sc[q] = __float_as_uint(s[(row >> 7) * m.scale_ld + (c >> 3)]);
+    } else if (FMT == OES_NVFP4) {
+      const uint16_t *s = reinterpret_cast<const uint16_t *>(m.scale + (int64_t)slot * m.scale_slot +
+                                                             (int64_t)row * m.scale_ld);
+      R.sc[q] = s[c];
+    } else {
+      R.sc[q] = 0;
+    }
+  }
+}
+
+template <int FMT, int G, int NQ>
 __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int RB) {
-  extern __shared__ __align__(16) uint16_t hs[];  // [k][I] bf16, then red[RB*k] floats
+  constexpr int EPC = Epc<FMT>::v;
+  constexpr int OPC = EPC / 8;                    // 16-byte operand vectors per chunk
+  constexpr int IB = NQ >= 4 ? 3 : (NQ == 3 ? 4 : (NQ == 2 ? 6 : 12));
+  constexpr int NSG = kThreads / G;
   const FfnArgs &a = ka.f;
   if (a.gate && *a.gate == 0) return;
   __shared__ int sl[32];
   __shared__ float wt[32];
+  __shared__ float red[kMaxRed];
   const int t = blockIdx.y;
-  const int k = a.k, I = a.I;
-  float *red = reinterpret_cast<float *>(hs + (int64_t)k * I);
+  const int k = a.k;
   if (threadIdx.x < k) {
     int s = a.slot_ids[(int64_t)t * k + threadIdx.x];
     if (s >= a.S) {
@@ -253,43 +304,55 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int RB) {
     wt[threadIdx.x] = a.w[(int64_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  const uint16_t *hsrc = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)t * k * I;
-  for (int j = 0; j < k; ++j)
-    if (sl[j] >= 0) stage_bf16(hs + (int64_t)j * I, hsrc + (int64_t)j * I, I);
-  __syncthreads();
-  constexpr int NSG = kThreads / G;
   const int sg = threadIdx.x / G, lg = threadIdx.x % G;
   const int r0 = blockIdx.x * RB;
   const int items = RB * k;
+  const int ips = (items + NSG - 1) / NSG;
+  const int i_end = min(items, (sg + 1) * ips);
   const Mat &m = ka.dn;
-  const int nqt = m.C / G;
-  for (int it0 = sg * kItemBatch; it0 < items; it0 += NSG * kItemBatch) {
-    float acc[kItemBatch];
-    int rows[kItemBatch], js[kItemBatch], slots[kItemBatch];
+  const uint16_t *hbase = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)t * k * a.I;
+  u32x4 hreg[NQ][OPC];
+  int cur_j = -1;
+  for (int i0 = sg * ips; i0 < i_end;) {
+    const int j = i0 / RB;
+    const int cnt = min(IB, min(i_end, (j + 1) * RB) - i0);
+    const int slot = sl[j];
+    float acc[IB];
 #pragma unroll
-    for (int b = 0; b < kItemBatch; ++b) {
-      const int it = it0 + b;
-      acc[b] = 0.f;
-      rows[b] = r0 + it / k;
-      js[b] = it % k;
-      slots[b] = (it < items && rows[b] < a.H) ? sl[js[b]] : -1;
+    for (int b = 0; b < IB; ++b) acc[b] = 0.f;
+    if (slot >= 0) {
+      if (j != cur_j) {
+        const u32x4 *hp = reinterpret_cast<const u32x4 *>(hbase + (int64_t)j * a.I);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+          for (int o = 0; o < OPC; ++o) hreg[q][o] = hp[(q * G + lg) * OPC + o];
+        cur_j = j;
+      }
+      RowN<NQ> R[IB];
+#pragma unroll
+      for (int b = 0; b < IB; ++b) {
+        const int row = r0 + (i0 + b) % RB;
+        if (b < cnt && row < a.H) load_row_n<FMT, G, NQ>(R[b], m, slot, row, lg);
+      }
+#pragma unroll
+      for (int b = 0; b < IB; ++b) {
+        const int row = r0 + (i0 + b) % RB;
+        if (b < cnt && row < a.H) {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) acc[b] += dot_chunk<FMT>(R[b].w[q], R[b].sc[q], hreg[q]);
+        }
+      }
     }
-    for (int q0 = 0; q0 < nqt; q0 += kMaxQ) {
-      const int nq = min(kMaxQ, nqt - q0);
-      RowRegs R[kItemBatch];
 #pragma unroll
-      for (int b = 0; b < kItemBatch; ++b)
-        if (slots[b] >= 0) load_row<FMT, G>(R[b], m, slots[b], rows[b], lg, q0, nq);
-#pragma unroll
-      for (int b = 0; b < kItemBatch; ++b)
-        if (slots[b] >= 0) acc[b] += dot_row<FMT, G>(R[b], hs + (int64_t)js[b] * I, lg, q0, nq);
+    for (int b = 0; b < IB; ++b) {
+      if (b < cnt) {
+        const float v = group_sum<G>(acc[b]);
+        const int row = r0 + (i0 + b) % RB;
+        if (lg == 0) red[i0 + b] = (slot >= 0 && row < a.H) ? v * row_global<FMT>(m, slot, row) : 0.f;
+      }
     }
-#pragma unroll
-    for (int b = 0; b < kItemBatch; ++b) {
-      const float v = group_sum<G>(acc[b]);
-      const int it = it0 + b;
-      if (lg == 0 && it < items) red[it] = slots[b] >= 0 ? v * row_global<FMT>(m, slots[b], rows[b]) : 0.f;
-    }
+    i0 += cnt;
   }
   __syncthreads();
   if (threadIdx.x < RB) {
@@ -297,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int RB) {
     if (row < a.H) {
       float s = 0.f;
       for (int j = 0; j < k; ++j)
-        if (sl[j] >= 0) s = fmaf(wt[j], red[threadIdx.x * k + j], s);
+        if (sl[j] >= 0) s = fmaf(wt[j], red[j * RB + threadIdx.x], s);
       a.y[(int64_t)t * a.H + row] = f32_to_bf16_rne(s);
     }
   }
@@ -359,15 +422,30 @@ hipError_t launch_gate_up_g(const KArgs &ka, hipStream_t s) {
   return hipGetLastError();
 }
 
+int down_rows_per_block(int H, int n) {
+  int rb = (int)std::min<int64_t>(16, std::max<int64_t>(1, (int64_t)H * n / 512));
+  while (rb & (rb - 1)) rb &= rb - 1;  // power of two
+  return rb;
+}
+
+template <int FMT, int G, int NQ>
+hipError_t launch_down_gq(const KArgs &ka, hipStream_t s) {
+  const FfnArgs &a = ka.f;
+  const int rb = down_rows_per_block(a.H, a.n);
+  dim3 grid((a.H + rb - 1) / rb, a.n);
+  hipLaunchKernelGGL((down_kernel<FMT, G, NQ>), grid, dim3(kThreads), 0, s, ka, rb);
+  return hipGetLastError();
+}
+
 template <int FMT, int G>
 hipError_t launch_down_g(const KArgs &ka, hipStream_t s) {
-  const FfnArgs &a = ka.f;
-  int rb = (int)std::min<int64_t>(16, std::max<int64_t>(1, (int64_t)a.H * a.n / 1024));
-  while (rb & (rb - 1)) rb &= rb - 1;  // power of two
-  dim3 grid((a.H + rb - 1) / rb, a.n);
-  const size_t lds = (size_t)a.k * a.I * 2 + (size_t)rb * a.k * 4;
-  hipLaunchKernelGGL((down_kernel<FMT, G>), grid, dim3(kThreads), lds, s, ka, rb);
-  return hipGetLastError();
+  switch (ka.dn.C / G) {
+    case 1: return launch_down_gq<FMT, G, 1>(ka, s);
+    case 2: return launch_down_gq<FMT, G, 2>(ka, s);
+    case 3: return launch_down_gq<FMT, G, 3>(ka, s);
+    case 4: return launch_down_gq<FMT, G, 4>(ka, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int FMT>
@@ -421,9 +499,11 @@ bool expert_ffn_supported(int format, int H, int I, int k) {
   const int epc = epc_of(format);
   if (!epc) return false;
   if (H % epc || I % epc) return false;
-  if (!pick_group(H / epc) || !pick_group(I / epc)) return false;
-  if (H > 16384) return false;                       // x row in LDS
-  if ((int64_t)k * I * 2 + 16 * k * 4 > 65536) return false;  // h rows of a token in LDS
+  const int gu = pick_group(H / epc), dn = pick_group(I / epc);
+  if (!gu || !dn) return false;
+  if ((I / epc) / dn > 4) return false;  // down: at most 4 chunks per lane held in registers
+  if (H > 16384) return false;          // x row staged in LDS by gate_up
+  if (k > 32 || 16 * k > kMaxRed) return false;
   return true;
 }
 

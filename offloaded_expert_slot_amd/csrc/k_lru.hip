@@ -18,8 +18,10 @@
 //   req[E]   u8   expert e of this layer requested
 //   emap[E]  i32  slot owning expert e of this layer, or -1
 //   mrank[E] i32  rank of expert e among the misses (exclusive scan)
-//   khi/klo[Spad] u64  victim keys, bitonic-sorted ascending; members of U and
-//                      padding get the all-ones key and sort last.
+//   khi/klo[Spad] u64  victim keys, bitonic-sorted ascending (keys live in
+//                      registers during the sort; LDS is the exchange buffer for
+//                      partners 64..kThreads-1 apart); members of U and padding
+//                      get the all-ones key and sort last.
 // Key encoding: khi = (owner != -1) << 63 | stamp  (stamps < 2^62),
 //               klo = (owner + 1) << 12 | slot     (owner < 2^50, slot < 4096).
 
@@ -63,6 +65,105 @@ __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
 
 __device__ inline bool key_less(uint64_t ah, uint64_t al, uint64_t bh, uint64_t bl) {
   return ah < bh || (ah == bh && al < bl);
+}
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int d) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Compare-exchange of element i (key a) against its partner (key b) in a
+// bitonic stage: keep the smaller key if i is the lower element of an
+// ascending pair or the upper element of a descending pair, else the larger.
+__device__ inline void keep(uint64_t &ah, uint64_t &al, uint64_t bh, uint64_t bl, bool take_min) {
+  const bool b_less = key_less(bh, bl, ah, al);
+  if (b_less == take_min) {
+    ah = bh;
+    al = bl;
+  }
+}
+
+// Bitonic sort (ascending) of Spad keys held R per thread: element i lives in
+// thread i % kThreads, register i / kThreads.  Partners closer than 64 are in
+// the same wave (cross-lane shuffle, no barrier); partners kThreads or more
+// apart are in the same thread; the rest go through LDS (xh / xl).
+template <int R>
+__device__ void bitonic_regs(uint64_t (&hi)[R], uint64_t (&lo)[R], int Spad, uint64_t *xh, uint64_t *xl) {
+  const int tid = threadIdx.x;
+  for (int kk = 2; kk <= Spad; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j >= kThreads) {
+        const int rj = j / kThreads;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int p = r ^ rj;
+          if (p > r && p < R) {
+            const int i = tid + r * kThreads;
+            const bool asc = (i & kk) == 0;
+            if (key_less(hi[p], lo[p], hi[r], lo[r]) == asc) {
+              const uint64_t th = hi[r], tl = lo[r];
+              hi[r] = hi[p]; lo[r] = lo[p];
+              hi[p] = th; lo[p] = tl;
+            }
+          }
+        }
+      } else if (j >= 64) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          xh[tid + r * kThreads] = hi[r];
+          xl[tid + r * kThreads] = lo[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int i = tid + r * kThreads;
+          const int p = i ^ j;
+          keep(hi[r], lo[r], xh[p], xl[p], ((i & j) == 0) == ((i & kk) == 0));
+        }
+        __syncthreads();
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int i = tid + r * kThreads;
+          const uint64_t ph = shfl_xor_u64(hi[r], j), pl = shfl_xor_u64(lo[r], j);
+          keep(hi[r], lo[r], ph, pl, ((i & j) == 0) == ((i & kk) == 0));
+        }
+      }
+    }
+  }
+}
+
+// Victim keys of the slots (members of U and padding get the all-ones key),
+// sorted ascending into khi / klo.
+template <int R>
+__device__ void sort_victims(const LruArgs &a, const uint8_t *req, int64_t base, uint64_t *khi, uint64_t *klo) {
+  uint64_t hi[R], lo[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int s = threadIdx.x + r * kThreads;
+    hi[r] = kMax;
+    lo[r] = kMax;
+    if (s < a.S) {
+      const int64_t o = a.owner[s];
+      const bool in_u = o >= base && o < base + a.E && req[(int)(o - base)];
+      if (!in_u) {
+        hi[r] = ((o != -1) ? (1ull << 63) : 0ull) | a.stamp[s];
+        lo[r] = ((uint64_t)(o + 1) << 12) | (uint64_t)s;
+      }
+    }
+  }
+  bitonic_regs<R>(hi, lo, a.Spad, khi, klo);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = threadIdx.x + r * kThreads;
+    if (i < a.Spad) {
+      khi[i] = hi[r];
+      klo[i] = lo[r];
+    }
+  }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
@@ -143,39 +244,13 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   }
 
   if (nM > 0) {
-    // 4. victim keys; slots holding a member of U are not evictable
-    for (int s = tid; s < a.Spad; s += kThreads) {
-      uint64_t hi = kMax, lo = kMax;
-      if (s < S) {
-        const int64_t o = a.owner[s];
-        const bool in_u = o >= base && o < base + E && req[(int)(o - base)];
-        if (!in_u) {
-          hi = ((o != -1) ? (1ull << 63) : 0ull) | a.stamp[s];
-          lo = ((uint64_t)(o + 1) << 12) | (uint64_t)s;
-        }
-      }
-      khi[s] = hi;
-      klo[s] = lo;
-    }
-    __syncthreads();
-    // 5. bitonic sort ascending
-    const int half = a.Spad >> 1;
-    for (int kk = 2; kk <= a.Spad; kk <<= 1) {
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < half; i += kThreads) {
-          const int lo_i = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-          const int hi_i = lo_i | j;
-          const bool asc = (lo_i & kk) == 0;
-          const uint64_t ah = khi[lo_i], al = klo[lo_i], bh = khi[hi_i], bl = klo[hi_i];
-          const bool gt = key_less(bh, bl, ah, al);
-          if (gt == asc) {
-            khi[lo_i] = bh; klo[lo_i] = bl;
-            khi[hi_i] = ah; klo[hi_i] = al;
-          }
-        }
-        __syncthreads();
-      }
-    }
+    // 4-5. victim keys sorted ascending (slots holding a member of U sort last)
+    if (a.Spad <= kThreads)
+      sort_victims<1>(a, req, base, khi, klo);
+    else if (a.Spad <= 2 * kThreads)
+      sort_victims<2>(a, req, base, khi, klo);
+    else
+      sort_victims<4>(a, req, base, khi, klo);
     // 6. install: the i-th miss takes the i-th victim
     for (int e = tid; e < E; e += kThreads) {
       const int r = mrank[e];
@@ -211,7 +286,14 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   }
 }
 
+__global__ void reset_step_kernel(Ctl *ctl) {
+  ctl->step_ok = 1;
+  ctl->miss_count = 0;
+}
+
 }  // namespace
+
+void launch_reset_step(Ctl *ctl, hipStream_t s) { hipLaunchKernelGGL(reset_step_kernel, dim3(1), dim3(1), 0, s, ctl); }
 
 hipError_t launch_lru_remap(const LruArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(lru_remap_kernel, dim3(1), dim3(kThreads), 0, s, a);

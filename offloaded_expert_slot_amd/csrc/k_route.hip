@@ -8,9 +8,9 @@
 //                    Wg [H, E] (bf16, row-major) against every token, fp32,
 //                    writing partial[s][t][e]; each thread owns one column pair
 //                    (a 4-byte load per row, coalesced along E).
-//   route_finish   - one workgroup per token: sums the partials in split order
-//                    (deterministic), writes the logits, picks the top-k by
-//                    repeated block argmax (larger logit first, lower index on
+//   route_finish   - one wave per token: sums the (at most 32) partials in split
+//                    order (deterministic), writes the logits, picks the top-k
+//                    by repeated wave argmax (larger logit first, lower index on
 //                    ties) and the softmax over the chosen logits.
 // route_logits runs route_finish alone on given logits (one split).
 
@@ -88,72 +88,73 @@ __device__ inline bool better(const Cand &a, const Cand &b) {  // a ranks before
   return a.v > b.v || (a.v == b.v && a.i < b.i);
 }
 
-__device__ inline Cand wave_best(Cand c) {
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) {
-    Cand o;
-    o.v = __shfl_xor(c.v, d, 64);
-    o.i = __shfl_xor(c.i, d, 64);
-    if (better(o, c)) c = o;
-  }
-  return c;
-}
+constexpr int kMaxPerLane = 8;  // E <= 512 experts over 64 lanes
 
-// One workgroup per token; E <= 512 so each thread owns at most two experts.
+// One wave per token: lane l owns experts l, l + 64, ...; the split partials are
+// summed in split order (deterministic), then k rounds of a wave-wide argmax
+// (larger logit first, lower index on ties) pick the top-k; lane j keeps the
+// j-th pick and writes its id and renormalised weight.
 __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float *partial, int splits, int n, int E,
                                                                      int k, float *logits, int32_t *ids, float *w) {
-  __shared__ Cand wbest[kRouteThreads / 64];
-  __shared__ float topv[32];
-  __shared__ int topi[32];
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float z[2];
-  bool taken[2] = {false, false};
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
+  if (t >= n) return;
+  const int64_t stride = (int64_t)n * E;
+  float z[kMaxPerLane];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = threadIdx.x + q * kRouteThreads;
+  for (int q = 0; q < kMaxPerLane; ++q) {
+    const int e = lane + 64 * q;
     float s = 0.f;
     if (e < E) {
-      for (int sp = 0; sp < splits; ++sp) s += partial[((int64_t)sp * n + t) * E + e];
+      const float *p = partial + (int64_t)t * E + e;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      int sp = 0;
+      for (; sp + 4 <= splits; sp += 4) {
+        a0 += p[(sp + 0) * stride];
+        a1 += p[(sp + 1) * stride];
+        a2 += p[(sp + 2) * stride];
+        a3 += p[(sp + 3) * stride];
+      }
+      for (; sp < splits; ++sp) a0 += p[sp * stride];
+      s = (a0 + a1) + (a2 + a3);
       if (logits) logits[(int64_t)t * E + e] = s;
     }
     z[q] = s;
   }
+  uint32_t taken = 0;
+  float myv = 0.f;
+  int myi = 0;
   for (int j = 0; j < k; ++j) {
     Cand c{-INFINITY, 0x7fffffff};
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = threadIdx.x + q * kRouteThreads;
-      if (e < E && !taken[q]) {
+    for (int q = 0; q < kMaxPerLane; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E && !((taken >> q) & 1u)) {
         Cand o{z[q], e};
         if (c.i == 0x7fffffff || better(o, c)) c = o;
       }
     }
-    c = wave_best(c);
-    if (lane == 0) wbest[wave] = c;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      Cand b = wbest[0];
-      for (int g = 1; g < kRouteThreads / 64; ++g)
-        if (wbest[g].i != 0x7fffffff && (b.i == 0x7fffffff || better(wbest[g], b))) b = wbest[g];
-      topv[j] = b.v;
-      topi[j] = b.i;
-    }
-    __syncthreads();
-    const int chosen = topi[j];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (threadIdx.x + q * kRouteThreads == chosen) taken[q] = true;
-  }
-  if (threadIdx.x == 0) {
-    const float m = topv[0];
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) s += expf(topv[j] - m);
-    const float inv = 1.f / s;
-    for (int j = 0; j < k; ++j) {
-      ids[(int64_t)t * k + j] = topi[j];
-      w[(int64_t)t * k + j] = expf(topv[j] - m) * inv;
+    for (int d = 32; d > 0; d >>= 1) {
+      Cand o;
+      o.v = __shfl_xor(c.v, d, 64);
+      o.i = __shfl_xor(c.i, d, 64);
+      if (o.i != 0x7fffffff && (c.i == 0x7fffffff || better(o, c))) c = o;
     }
+    if ((c.i & 63) == lane) taken |= 1u << (c.i >> 6);
+    if (lane == j) {
+      myv = c.v;
+      myi = c.i;
+    }
+  }
+  const float v0 = __shfl(myv, 0, 64);
+  const float ex = lane < k ? expf(myv - v0) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = myi;
+    w[(int64_t)t * k + lane] = ex / sum;
   }
 }
 
@@ -161,15 +162,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float
 
 int route_splits(int H, int E) {
   const int rpp = kRouteThreads / (E / 2);
-  // aim for ~4 rows per thread group per split, at most 256 splits
-  int rows = std::max(rpp * 4, (H + 255) / 256);
+  // at most 32 splits (the finishing wave sums them), each a multiple of rpp rows
+  int rows = std::max(rpp, (H + 31) / 32);
   rows = (rows + rpp - 1) / rpp * rpp;
   return (H + rows - 1) / rows;
 }
 
 static int route_rows_per_split(int H, int E) {
-  const int splits = route_splits(H, E);
-  return (H + splits - 1) / splits;
+  const int rpp = kRouteThreads / (E / 2);
+  int rows = std::max(rpp, (H + 31) / 32);
+  return (rows + rpp - 1) / rpp * rpp;
 }
 
 hipError_t launch_route(const uint16_t *x, const uint16_t *wg, int n, int H, int E, int k, int32_t *ids, float *w,
@@ -180,13 +182,13 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *wg, int n, int H, int
                      reinterpret_cast<const uint32_t *>(wg), n, H, E, rows, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_finish_kernel, dim3(n), dim3(kRouteThreads), 0, s, partial, splits, n, E, k, logits, ids,
-                     w);
+  hipLaunchKernelGGL(route_finish_kernel, dim3((n + 3) / 4), dim3(kRouteThreads), 0, s, partial, splits, n, E, k, logits,
+                     ids, w);
   return hipGetLastError();
 }
 
 hipError_t launch_route_logits(const float *logits, int n, int E, int k, int32_t *ids, float *w, hipStream_t s) {
-  hipLaunchKernelGGL(route_finish_kernel, dim3(n), dim3(kRouteThreads), 0, s, logits, 1, n, E, k,
+  hipLaunchKernelGGL(route_finish_kernel, dim3((n + 3) / 4), dim3(kRouteThreads), 0, s, logits, 1, n, E, k,
                      static_cast<float *>(nullptr), ids, w);
   return hipGetLastError();
 }

@@ -33,6 +33,8 @@ struct LruArgs {
   int64_t bpe;
 };
 hipError_t launch_lru_remap(const LruArgs &a, hipStream_t s);
+// step_ok = 1, miss_count = 0 (a one-thread kernel, safe under graph capture)
+void launch_reset_step(Ctl *ctl, hipStream_t s);
 
 // ---------------------------------------------------------------- copy (gather)
 struct CopyBank {
@@ -94,6 +96,7 @@ struct PrefillArgs {
   uint8_t *ws;                // workspace
   int64_t ws_bytes;
 };
+bool prefill_supported(int H, int I, int E);
 int64_t prefill_workspace_bytes(int H, int I, int n, int k, int E);
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s);
 

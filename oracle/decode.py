@@ -79,3 +79,12 @@ def fp4x2_unpack(packed):
     out[..., 0::2] = p & 0xF
     out[..., 1::2] = p >> 4
     return out
+
+
+def via_table(fn, codes, ncodes):
+    """fn applied to integer codes by evaluating fn once on every possible code.
+
+    Same values as fn(codes); used for large arrays of 4- and 8-bit codes.
+    """
+    table = fn(np.arange(ncodes))
+    return table[np.asarray(codes).astype(np.intp)]

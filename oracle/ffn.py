@@ -43,7 +43,7 @@ def _bf16_matrix(raw, shape):
 
 
 def _fp8_matrix(raw_q, shape, raw_s, sshape):
-    q = decode.e4m3(raw_q.reshape(shape))
+    q = decode.via_table(decode.e4m3, raw_q.reshape(shape), 256)
     s = raw_s.view(np.float32).reshape(sshape).astype(np.float64)
     return q * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
 
@@ -51,8 +51,8 @@ def _fp8_matrix(raw_q, shape, raw_s, sshape):
 def _nvfp4_matrix(raw_c, cshape, raw_s, sshape, raw_g):
     rows, half = cshape
     codes = decode.fp4x2_unpack(raw_c.reshape(rows, half))          # [rows, K]
-    vals = decode.e2m1(codes)
-    sc = decode.e4m3(raw_s.reshape(sshape))                          # [rows, K/16]
+    vals = decode.via_table(decode.e2m1, codes, 16)
+    sc = decode.via_table(decode.e4m3, raw_s.reshape(sshape), 256)   # [rows, K/16]
     g = decode.fp16(raw_g.view(np.uint16))                           # [rows]
     return vals * np.repeat(sc, 16, axis=1) * g[:, None]
 
@@ -61,7 +61,7 @@ def _mxfp4_matrix(raw_b, bshape, raw_s, sshape):
     kb, n, _ = bshape
     blocks = raw_b.reshape(bshape)                                   # [K/32, N, 16]
     codes = decode.fp4x2_unpack(blocks)                              # [K/32, N, 32]
-    vals = decode.e2m1(codes) * decode.e8m0(raw_s.reshape(sshape))[:, :, None]
+    vals = decode.via_table(decode.e2m1, codes, 16) * decode.e8m0(raw_s.reshape(sshape))[:, :, None]
     # W[n, c] with c = 32 * kb + position in block
     return vals.transpose(1, 0, 2).reshape(n, kb * 32)
 

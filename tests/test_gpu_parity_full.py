@@ -1,0 +1,169 @@
+"""GPU parity against the oracle at the decode workloads' full sizes.
+
+For each decode workload (bf16 H=2048, fp8-block H=4096, nvfp4 H=7168; full
+expert count, full slot pool with every slot owned by another layer):
+
+* copy-sweep rows run through ensure_experts + copy_missing exactly as the
+  benchmark times them; the slot map and miss list must equal the oracle LRU's,
+  every touched slot must hold the host row byte for byte, sampled untouched
+  slots must still hold the sentinel;
+* the bs=1 decode step (route -> ensure -> copy -> FFN) must match the oracle:
+  slot map and misses exactly, y to the relative-L2 bound of the format.
+"""
+import numpy as np
+import pytest
+import torch
+
+import offloaded_expert_slot_amd as oes
+import synth
+from oracle import ffn as offn
+from oracle import formulas
+from oracle import route as oroute
+from oracle.lru import OK, SlotTable
+from synth.workloads import WORKLOADS, make_host_banks
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+_STATE = {}
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _setup(name):
+    if _STATE.get("name") != name:
+        _STATE.clear()
+        torch.cuda.empty_cache()
+        w = WORKLOADS[name]
+        hb = make_host_banks(w)
+        sc = oes.schema_make(w.fmt, w.L, w.E, w.H, w.I)
+        c = oes.Cache(sc, w.S, 0)
+        for b, t in enumerate(hb.banks):
+            c.set_source(b, 0, t)
+        _STATE.update(name=name, w=w, hb=hb, c=c, sc=sc)
+    return _STATE["w"], _STATE["hb"], _STATE["c"]
+
+
+SWEEP_ROWS = [("bf16_h2048", 8, 0.5), ("bf16_h2048", 32, 1.0), ("bf16_h2048", 1, 0.25),
+              ("fp8_h4096", 16, 0.1), ("fp8_h4096", 1, 0.5),
+              ("nvfp4_h7168", 4, 0.25), ("nvfp4_h7168", 1, 0.05), ("nvfp4_h7168", 4, 1.0)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,bs,mr", SWEEP_ROWS)
+@pytest.mark.parametrize("fused", [1, 0])
+def test_copy_sweep_row(name, bs, mr, fused):
+    w, hb, c = _setup(name)
+    _case(f"copy sweep {name} bs={bs} mr={mr} fused={fused}")
+    c.set_option(oes.OPT_FUSED_COPY, fused)
+    ids = synth.synthetic_ids(bs, w.k, w.E, 0, w.name).numpy()
+    active = formulas.active_unique(bs, w.k, w.E)
+    assert len(set(ids.ravel().tolist())) == active
+    m = formulas.num_misses(active, mr)
+    owner, stamp, clock, _ = synth.forced_miss_state(w.S, w.E, 0, ids, m)
+    c.fill_slots(0xA5)
+    c.set_state(owner, stamp, clock)
+    d_ids = torch.from_numpy(ids).to(G.dev())
+    d_slots = torch.empty_like(d_ids)
+    c.ensure_experts(0, d_ids, d_slots)
+    c.copy_missing()
+    torch.cuda.synchronize()
+    c.check()
+    t = SlotTable(w.S, w.L, w.E)
+    t.set_state(owner, stamp, clock)
+    r = t.ensure(0, ids)
+    assert r.status == OK and len(r.misses) == m
+    assert np.array_equal(d_slots.cpu().numpy(), r.slot_ids)
+    assert c.get_misses() == r.misses
+    got_owner, _, _ = c.get_state()
+    assert np.array_equal(got_owner, t.owner)
+    touched = {s for s, _ in r.misses}
+    rng = np.random.default_rng(0)
+    untouched = [int(s) for s in rng.choice(w.S, size=24, replace=False) if int(s) not in touched]
+    for b in range(len(hb.banks)):
+        view = c.slot_bank_view(b)
+        for s, fid in r.misses:
+            assert torch.equal(view[s].cpu(), hb.row(b, fid)), (b, s, fid)
+        for s in untouched:
+            assert bool((view[s] == 0xA5).all()), (b, s)
+    c.set_option(oes.OPT_FUSED_COPY, 1)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,mr", [("bf16_h2048", 0.5), ("fp8_h4096", 0.5), ("nvfp4_h7168", 0.25)])
+def test_decode_step_bs1(name, mr):
+    w, hb, c = _setup(name)
+    _case(f"decode step {name} bs=1 mr={mr}")
+    dev = G.dev()
+    x = synth.activations(1, w.H, 0, w.name).to(dev)
+    wg = synth.router_weight(w.H, w.E, 0, w.name).to(dev)
+    ids = torch.empty((1, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, w.k), dtype=torch.float32, device=dev)
+    oes.route(x, wg, w.k, ids, wts, torch.empty(oes.route_workspace_bytes(1, w.H, w.E), dtype=torch.uint8,
+                                                  device=dev))
+    torch.cuda.synchronize()
+    # the routed ids are the oracle router's; the GPU router must agree on them
+    routed, ow, _ = oroute.route(G.bits16(x), G.bits16(wg), w.k)
+    assert np.array_equal(ids.cpu().numpy(), routed)
+    np.testing.assert_allclose(wts.cpu().numpy(), ow, rtol=2e-4, atol=1e-6)
+    m = formulas.num_misses(len(set(routed.ravel().tolist())), mr)
+    owner, stamp, clock, pre = synth.forced_miss_state(w.S, w.E, 0, routed, m)
+    c.set_state(owner, stamp, clock)
+    if pre:
+        c.load_rows([p[0] for p in pre], [p[1] for p in pre])
+    slot_ids = torch.empty_like(ids)
+    y = torch.empty((1, w.H), dtype=torch.int16, device=dev)
+    ws = torch.empty(c.ffn_workspace_bytes(1, w.k), dtype=torch.uint8, device=dev)
+    c.ensure_experts(0, ids, slot_ids)
+    c.copy_missing()
+    c.expert_ffn(x, slot_ids, wts, y, ws)
+    torch.cuda.synchronize()
+    c.check()
+    t = SlotTable(w.S, w.L, w.E)
+    t.set_state(owner, stamp, clock)
+    r = t.ensure(0, routed)
+    assert np.array_equal(slot_ids.cpu().numpy(), r.slot_ids)
+    assert c.get_misses() == r.misses and len(r.misses) == m
+    # the oracle reads each slot's expert from the host banks by the slot's owner
+    ref = offn.expert_ffn(w.fmt, w.H, w.I, G.bits16(x), r.slot_ids, ow,
+                          lambda s: [hb.row(b, int(t.owner[s]) % w.E).numpy() for b in range(len(hb.banks))])
+    err = offn.rel_l2(G.bf16_tensor_to_f64(y), ref)
+    print(f"  rel_l2={err:.3e}")
+    assert err <= (3e-2 if w.fmt == "nvfp4" else 1e-2)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,bs,tokens", [("bf16_h2048", 8, None), ("bf16_h2048", 32, (0, 31)),
+                                            ("fp8_h4096", 16, (3,)), ("nvfp4_h7168", 4, (1,))])
+def test_decode_ffn_batched(name, bs, tokens):
+    """Batched FFN on routed ids; the oracle checks all tokens or a sample of them."""
+    w, hb, c = _setup(name)
+    _case(f"ffn {name} bs={bs}")
+    dev = G.dev()
+    x = synth.activations(bs, w.H, 0, w.name, step=7).to(dev)
+    wg = synth.router_weight(w.H, w.E, 0, w.name).to(dev)
+    oids, ow, _ = oroute.route(G.bits16(x), G.bits16(wg), w.k)
+    ids = torch.from_numpy(oids).to(dev)
+    wts = torch.from_numpy(ow.astype(np.float32)).to(dev)
+    owner, stamp, clock = synth.foreign_state(w.S, w.E)
+    c.set_state(owner, stamp, clock)
+    slot_ids = torch.empty_like(ids)
+    y = torch.empty((bs, w.H), dtype=torch.int16, device=dev)
+    ws = torch.empty(c.ffn_workspace_bytes(bs, w.k), dtype=torch.uint8, device=dev)
+    c.ensure_experts(0, ids, slot_ids)
+    c.copy_missing()
+    c.expert_ffn(x, slot_ids, wts, y, ws)
+    torch.cuda.synchronize()
+    c.check()
+    t = SlotTable(w.S, w.L, w.E)
+    t.set_state(owner, stamp, clock)
+    r = t.ensure(0, oids)
+    assert np.array_equal(slot_ids.cpu().numpy(), r.slot_ids)
+    sel = list(range(bs)) if tokens is None else list(tokens)
+    ref = offn.expert_ffn(w.fmt, w.H, w.I, G.bits16(x)[sel], r.slot_ids[sel], ow[sel].astype(np.float32).astype(np.float64),
+                          lambda s: [hb.row(b, int(t.owner[s]) % w.E).numpy() for b in range(len(hb.banks))])
+    err = offn.rel_l2(G.bf16_tensor_to_f64(y)[sel], ref)
+    print(f"  rel_l2={err:.3e}")
+    assert err <= (3e-2 if w.fmt == "nvfp4" else 1e-2)

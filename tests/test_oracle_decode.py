@@ -65,3 +65,12 @@ def test_fp4x2_unpack_order():
     # reading: element 2j in the low nibble of byte j
     codes = decode.fp4x2_unpack(np.array([[0x21, 0xF7]], dtype=np.uint8))
     assert codes.tolist() == [[1, 2, 7, 15]]
+
+
+def test_table_evaluation_equals_direct():
+    rng = np.random.default_rng(4)
+    b = rng.integers(0, 256, size=(7, 33), dtype=np.uint8)
+    for fn, n in ((decode.e4m3, 256), (decode.e8m0, 256)):
+        _same(decode.via_table(fn, b, n), fn(b))
+    c = rng.integers(0, 16, size=(5, 9))
+    _same(decode.via_table(decode.e2m1, c, 16), decode.e2m1(c))
