@@ -19,7 +19,8 @@ Also printed (same JSON line): the copy sweep of the benchmark guide's columns
 25 event-timed ensure+copy repeats, fused and per-bank), decode tok/s at every
 miss rate, the measured ceilings (pinned H2D by DMA and by the zero-copy
 kernel, HBM streaming read), the roofline of the dominant kernel and of the
-FFN, and the CPU oracle timed on this host.
+FFN, the MXFP4 prefill layer (grouped FFN on MFMA, whole-layer stream, the
+overlapped loop over 4 layers) and the CPU oracle timed on this host.
 """
 import argparse
 import json
@@ -35,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "copy_missing GB/s + tok_ms per miss rate; MoE-layer decode tok/s at bs=1"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 PCIE_PEAK_GBS = 64.0         # PCIe 5.0 x16, one direction, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
 def parse():
@@ -49,6 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill (MXFP4 layer stream) part")
     return ap.parse_args()
 
 
@@ -235,6 +238,15 @@ def main():
     roof = {"kernel": dominant, "bound": roof["bound"], "achieved": roof["achieved"], "peak": roof["peak"],
             "unit": roof["unit"], "frac": roof["frac"], "traffic": roof["traffic"]}
 
+    # ---------------------------------------------------------------- prefill (MXFP4 layer stream)
+    prefill = None
+    if not args.no_prefill:
+        prefill = _prefill(WORKLOADS["mxfp4_prefill"], log)
+        kernels["prefill_ffn"] = {"bound": "mfma", "achieved": prefill["ffn_TFLOPs"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": prefill["ffn_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS,
+                                  "flops_per_launch": prefill["flops"], "avg_ms": prefill["ffn_ms"],
+                                  "hbm_GBps": prefill["ffn_weight_GBps"], "traffic": None}
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -251,10 +263,72 @@ def main():
                    "misses": head["misses"], "active": active, "bytes_per_expert": bpe},
         "tok_ms": head["tok_ms"], "copy_GBps": head.get("copy_GBps"),
         "roofline": roof, "kernels": kernels, "probes": probes, "decode_per_miss_rate": per_mr,
-        "copy_sweep": sweep, "cpu_baseline": cpu,
+        "copy_sweep": sweep, "prefill": prefill, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     cache.close()
+
+
+def _prefill(w, log):
+    """MXFP4 prefill: grouped FFN time (MFMA), one layer's stream time, and the overlapped loop."""
+    import numpy as np
+    import torch
+
+    import offloaded_expert_slot_amd as oes
+    import synth
+    from synth.workloads import make_host_banks
+
+    dev = torch.device("cuda:0")
+    hb = make_host_banks(w)
+    sc = oes.schema_make(w.fmt, w.stream_layers, w.E, w.H, w.I)
+    L = oes.Layers(sc, 2, 0)
+    for layer in range(w.stream_layers):
+        for b, t in enumerate(hb.banks):
+            L.set_source(b, layer, t)   # one host bank reused under every layer id
+    L.prefetch(0)
+    logits = synth.router_logits(w.tokens, w.E, 0, w.name).to(dev)
+    ids = torch.empty((w.tokens, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.tokens, w.k), dtype=torch.float32, device=dev)
+    oes.route_logits(logits, w.k, ids, wts)
+    x = synth.activations(w.tokens, w.H, 0, w.name).to(dev)
+    y = torch.empty((w.tokens, w.H), dtype=torch.int16, device=dev)
+    ws = torch.empty(L.ffn_workspace_bytes(w.tokens, w.k), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        L.ffn(0, x, ids, wts, y, ws)
+    marks = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.ffn(0, x, ids, wts, y, ws)
+        b.record()
+        marks.append((a, b))
+    torch.cuda.synchronize()
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
+    flops = 6.0 * w.tokens * w.k * w.H * w.I
+    wbytes = w.E * sc.bytes_per_expert
+    cs = torch.cuda.Stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(cs)
+    L.prefetch(1, cs)
+    b.record(cs)
+    b.synchronize()
+    copy_ms = a.elapsed_time(b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    L.prefetch(0, cs)
+    for layer in range(w.stream_layers):
+        if layer + 1 < w.stream_layers:
+            L.prefetch(layer + 1, cs)
+        L.ffn(layer, x, ids, wts, y, ws)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0
+    out = {"workload": w.name, "tokens": w.tokens, "flops": flops, "ffn_ms": ffn_ms,
+           "ffn_TFLOPs": flops / (ffn_ms * 1e9), "ffn_weight_GBps": wbytes / (ffn_ms * 1e6),
+           "layer_bytes": wbytes, "layer_copy_ms": copy_ms, "stream_GBps": wbytes / (copy_ms * 1e6),
+           "layers": w.stream_layers, "overlapped_ms_per_layer": wall_ms / w.stream_layers}
+    log("prefill", {k: (round(v, 3) if isinstance(v, float) else v) for k, v in out.items()})
+    L.close()
+    return out
 
 
 def _cpu_baseline(w, hb, x, wg, mr, budget_s):
