@@ -196,7 +196,8 @@ oes_status oes_cache_check(oes_cache *c, void *stream);
  * at creation).  OES_OPT_COPY_MODE: OES_COPY_ZERO (default) the gather
  * kernel reads mapped pinned memory; OES_COPY_SDMA copy_missing syncs the
  * stream, reads the miss list and issues one DMA copy per (miss, bank)
- * (default from env OES_COPY_MODE=zerocopy|sdma). */
+ * (default from env OES_COPY_MODE=zerocopy|sdma).  OES_OPT_COPY_BLOCKS: grid
+ * size of the gather (0 = default). */
 enum { OES_OPT_FUSED_COPY = 1, OES_OPT_COPY_MODE = 2, OES_OPT_COPY_BLOCKS = 3 };
 enum { OES_COPY_ZERO = 0, OES_COPY_SDMA = 1 };
 oes_status oes_cache_set_option(oes_cache *c, int32_t option, int64_t value);

@@ -78,15 +78,20 @@ struct Mat {
   int32_t rows, K, C;     // C = chunks per row
 };
 
-// Registers of one row's chunks (this lane's share).
+// Registers of one row's chunks (this lane's share), and the row's nvfp4 global.
 struct RowRegs {
   u32x4 w[kMaxQ];
   uint32_t sc[kMaxQ];
+  float gl;
 };
+
+template <int FMT>
+__device__ inline float row_global(const Mat &m, int slot, int row);
 
 template <int FMT, int G>
 __device__ inline void load_row(RowRegs &R, const Mat &m, int slot, int row, int lg, int q0, int nq) {
   const u32x4 *p = reinterpret_cast<const u32x4 *>(m.codes + (int64_t)slot * m.codes_slot + (int64_t)row * m.row_bytes);
+  R.gl = row_global<FMT>(m, slot, row);  // issued with the weights, used after the lane reduction
 #pragma unroll
   for (int q = 0; q < kMaxQ; ++q) {
     if (q < nq) {
@@ -184,6 +189,29 @@ __device__ inline float group_sum(float v) {
   return v;
 }
 
+// Sums V per-lane values (V items) over a subgroup of G lanes (V <= G, both powers
+// of two) with a butterfly that halves the values at every step: (V - 1) +
+// log2(G / V) shuffles instead of V * log2(G).  Afterwards the lanes
+// [i * G / V, (i + 1) * G / V) of the subgroup all hold the total of item i.
+template <int G, int V>
+__device__ inline float group_sum_multi(float (&v)[V], int lg) {
+  static_assert(V >= 1 && V <= G && (V & (V - 1)) == 0, "V must be a power of two <= G");
+#pragma unroll
+  for (int h = V / 2, d = G / 2; h >= 1; h >>= 1, d >>= 1) {
+    const bool upper = (lg & d) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float send = upper ? v[i] : v[i + h];
+      const float keep = upper ? v[i + h] : v[i];
+      v[i] = keep + __shfl_xor(send, d, G);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int d = G / V / 2; d > 0; d >>= 1) r += __shfl_xor(r, d, G);
+  return r;
+}
+
 template <int FMT>
 __device__ inline float row_global(const Mat &m, int slot, int row) {
   if (FMT == OES_NVFP4) {
@@ -227,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
   const int r = blockIdx.x * NSG + sg;
   if (r >= a.I) return;
   const Mat &m = ka.gu;
-  float g = 0.f, u = 0.f;
+  float g = 0.f, u = 0.f, gg = 1.f, gu = 1.f;
   for (int q0 = 0; q0 * G < m.C; q0 += kMaxQ) {
     const int nq = min(kMaxQ, m.C / G - q0);
     RowRegs Rg, Ru;
@@ -235,12 +263,15 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
     load_row<FMT, G>(Ru, m, slot, a.I + r, lg, q0, nq);
     g += dot_row<FMT, G>(Rg, xs, lg, q0, nq);
     u += dot_row<FMT, G>(Ru, xs, lg, q0, nq);
+    gg = Rg.gl;
+    gu = Ru.gl;
   }
-  g = group_sum<G>(g);
-  u = group_sum<G>(u);
+  float gu2[2] = {g * gg, u * gu};
+  const float tot = group_sum_multi<G, 2>(gu2, lg);  // lanes [0, G/2): gate, [G/2, G): up
+  const float other = __shfl_xor(tot, G / 2, G);
   if (lg == 0) {
-    g *= row_global<FMT>(m, slot, r);
-    u *= row_global<FMT>(m, slot, a.I + r);
+    g = tot;
+    u = other;
     const float hv = g / (1.f + __expf(-g)) * u;
     reinterpret_cast<uint16_t *>(a.h)[(int64_t)p * a.I + r] = f32_to_bf16_rne(hv);
   }
@@ -255,67 +286,47 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
 // (deterministic) and written as bf16.
 constexpr int kMaxRed = 512;  // RB * k partial results per block (RB <= 16, k <= 32)
 
-template <int NQ>
-struct RowN {
-  u32x4 w[NQ];
-  uint32_t sc[NQ];
-};
 
 template <int FMT, int G, int NQ>
-__device__ inline void load_row_n(RowN<NQ> &R, const Mat &m, int slot, int row, int lg) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(m.codes + (int64_t)slot * m.codes_slot + (int64_t)row * m.row_bytes);
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int c = q * G + lg;
-    R.w[q] = __builtin_nontemporal_load(p + c);
-    if (FMT == OES_FP8_BLOCK128) {
-      const float *s = reinterpret_cast<const float *>(m.scale + (int64_t)slot * m.scale_slot);
-      R.sc[q] = __float_as_uint(s[(row >> 7) * m.scale_ld + (c >> 3)]);
-    } else if (FMT == OES_NVFP4) {
-      const uint16_t *s = reinterpret_cast<const uint16_t *>(m.scale + (int64_t)slot * m.scale_slot +
-                                                             (int64_t)row * m.scale_ld);
-      R.sc[q] = s[c];
-    } else {
-      R.sc[q] = 0;
-    }
-  }
-}
-
-template <int FMT, int G, int NQ>
-__global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int RB) {
+__global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int lrb) {
   constexpr int EPC = Epc<FMT>::v;
-  constexpr int OPC = EPC / 8;                    // 16-byte operand vectors per chunk
-  constexpr int IB = NQ >= 4 ? 3 : (NQ == 3 ? 4 : (NQ == 2 ? 6 : 12));
+  constexpr int OPC = EPC / 8;                           // 16-byte operand vectors per chunk
+  constexpr int IB0 = NQ >= 2 ? 4 : 8;                  // rows per batch (a power of two)
+  constexpr int IB = IB0 < G ? IB0 : G;
   constexpr int NSG = kThreads / G;
   const FfnArgs &a = ka.f;
   if (a.gate && *a.gate == 0) return;
   __shared__ int sl[32];
   __shared__ float wt[32];
   __shared__ float red[kMaxRed];
+  const int RB = 1 << lrb;                               // rows per block (a power of two)
   const int t = blockIdx.y;
   const int k = a.k;
   if (threadIdx.x < k) {
-    int s = a.slot_ids[(int64_t)t * k + threadIdx.x];
+    int s = a.slot_ids[t * k + threadIdx.x];
     if (s >= a.S) {
       atomicCAS(a.err, 0, (int)OES_ERR_ARG);
       s = -1;
     }
     sl[threadIdx.x] = s;
-    wt[threadIdx.x] = a.w[(int64_t)t * k + threadIdx.x];
+    wt[threadIdx.x] = a.w[t * k + threadIdx.x];
   }
   __syncthreads();
   const int sg = threadIdx.x / G, lg = threadIdx.x % G;
-  const int r0 = blockIdx.x * RB;
-  const int items = RB * k;
+  const int r0 = blockIdx.x << lrb;
+  const int items = k << lrb;                            // (pair j, row) items, pair-major
   const int ips = (items + NSG - 1) / NSG;
   const int i_end = min(items, (sg + 1) * ips);
   const Mat &m = ka.dn;
   const uint16_t *hbase = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)t * k * a.I;
+  const uint32_t row_bytes = (uint32_t)m.row_bytes;
+  const uint32_t scale_ld = (uint32_t)m.scale_ld;
   u32x4 hreg[NQ][OPC];
   int cur_j = -1;
   for (int i0 = sg * ips; i0 < i_end;) {
-    const int j = i0 / RB;
-    const int cnt = min(IB, min(i_end, (j + 1) * RB) - i0);
+    const int j = i0 >> lrb;
+    const int row0 = r0 + (i0 & (RB - 1));               // rows of a batch are consecutive
+    const int cnt = min(IB, min(i_end, (j + 1) << lrb) - i0);
     const int slot = sl[j];
     float acc[IB];
 #pragma unroll
@@ -329,28 +340,47 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int RB) {
           for (int o = 0; o < OPC; ++o) hreg[q][o] = hp[(q * G + lg) * OPC + o];
         cur_j = j;
       }
-      RowN<NQ> R[IB];
+      // per-batch bases; per-row offsets stay 32-bit
+      const uint8_t *cb = m.codes + (int64_t)slot * m.codes_slot;
+      const uint8_t *sb = FMT == OES_BF16 ? nullptr : m.scale + (int64_t)slot * m.scale_slot;
+      const uint16_t *gb = FMT == OES_NVFP4 ? reinterpret_cast<const uint16_t *>(m.glob + (int64_t)slot * m.glob_slot)
+                                            : nullptr;
+      u32x4 w[IB][NQ];
+      uint32_t sc[IB][NQ];
+      float gl[IB];
 #pragma unroll
       for (int b = 0; b < IB; ++b) {
-        const int row = r0 + (i0 + b) % RB;
-        if (b < cnt && row < a.H) load_row_n<FMT, G, NQ>(R[b], m, slot, row, lg);
+        const int row = row0 + b;
+        gl[b] = 1.f;
+        if (b < cnt && row < a.H) {
+          const u32x4 *p = reinterpret_cast<const u32x4 *>(cb + (uint32_t)row * row_bytes);
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const int c = q * G + lg;
+            w[b][q] = __builtin_nontemporal_load(p + c);
+            if (FMT == OES_FP8_BLOCK128)
+              sc[b][q] = reinterpret_cast<const uint32_t *>(sb)[(uint32_t)(row >> 7) * scale_ld + (c >> 3)];
+            else if (FMT == OES_NVFP4)
+              sc[b][q] = reinterpret_cast<const uint16_t *>(sb + (uint32_t)row * scale_ld)[c];
+            else
+              sc[b][q] = 0;
+          }
+          if (FMT == OES_NVFP4) gl[b] = fp16_to_f32(gb[row]);
+        }
       }
 #pragma unroll
       for (int b = 0; b < IB; ++b) {
-        const int row = r0 + (i0 + b) % RB;
-        if (b < cnt && row < a.H) {
+        if (b < cnt && row0 + b < a.H) {
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) acc[b] += dot_chunk<FMT>(R[b].w[q], R[b].sc[q], hreg[q]);
+          for (int q = 0; q < NQ; ++q) acc[b] += dot_chunk<FMT>(w[b][q], sc[b][q], hreg[q]);
+          acc[b] *= gl[b];  // the row's global multiplies every lane's partial sum
         }
       }
     }
-#pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      if (b < cnt) {
-        const float v = group_sum<G>(acc[b]);
-        const int row = r0 + (i0 + b) % RB;
-        if (lg == 0) red[i0 + b] = (slot >= 0 && row < a.H) ? v * row_global<FMT>(m, slot, row) : 0.f;
-      }
+    const float v = group_sum_multi<G, IB>(acc, lg);   // item lg / (G / IB)
+    if (lg % (G / IB) == 0) {
+      const int b = lg / (G / IB);
+      if (b < cnt) red[i0 + b] = (slot >= 0 && row0 + b < a.H) ? v : 0.f;
     }
     i0 += cnt;
   }
@@ -359,8 +389,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int RB) {
     const int row = r0 + threadIdx.x;
     if (row < a.H) {
       float s = 0.f;
-      for (int j = 0; j < k; ++j)
-        if (sl[j] >= 0) s = fmaf(wt[j], red[j * RB + threadIdx.x], s);
+      for (int jj = 0; jj < k; ++jj)
+        if (sl[jj] >= 0) s = fmaf(wt[jj], red[(jj << lrb) + threadIdx.x], s);
       a.y[(int64_t)t * a.H + row] = f32_to_bf16_rne(s);
     }
   }
@@ -373,6 +403,25 @@ int pick_group(int C) {
   if (C % 16 == 0) return 16;
   if (C % 8 == 0) return 8;
   return 0;
+}
+
+// down subgroups: at least one subgroup per routed pair (G <= 256 / k), each lane
+// holding at most 4 chunks of a row, so a block's rows x pairs split into one
+// batch per subgroup.
+int pick_group_dn(int C, int k) {
+  for (int g = 64; g >= 8; g /= 2)
+    if (C % g == 0 && C / g <= 4 && g * k <= kThreads) return g;
+  for (int g = 64; g >= 8; g /= 2)
+    if (C % g == 0 && C / g <= 4) return g;
+  return 0;
+}
+
+// gate_up subgroups: the smallest G whose share is at most kMaxQ chunks per lane,
+// so each lane keeps up to 2 x kMaxQ 16-byte loads (gate and up rows) in flight.
+int pick_group_gu(int C) {
+  for (int g = 8; g <= 64; g *= 2)
+    if (C % g == 0 && C / g <= kMaxQ) return g;
+  return pick_group(C);
 }
 
 int epc_of(int fmt) {
@@ -422,18 +471,24 @@ hipError_t launch_gate_up_g(const KArgs &ka, hipStream_t s) {
   return hipGetLastError();
 }
 
-int down_rows_per_block(int H, int n) {
-  int rb = (int)std::min<int64_t>(16, std::max<int64_t>(1, (int64_t)H * n / 512));
-  while (rb & (rb - 1)) rb &= rb - 1;  // power of two
+// Rows per block: enough that every subgroup gets one full batch of IB rows of
+// one pair (RB * k = subgroups * IB), a power of two in [1, 16].
+int down_rows_per_block(int G, int NQ, int k) {
+  const int ib0 = NQ >= 2 ? 4 : 8;
+  const int ib = ib0 < G ? ib0 : G;
+  int rb = std::max(1, std::min(16, ib * (kThreads / G) / k));
+  while (rb & (rb - 1)) rb &= rb - 1;
   return rb;
 }
 
 template <int FMT, int G, int NQ>
 hipError_t launch_down_gq(const KArgs &ka, hipStream_t s) {
   const FfnArgs &a = ka.f;
-  const int rb = down_rows_per_block(a.H, a.n);
+  const int rb = down_rows_per_block(G, NQ, a.k);
+  int lrb = 0;
+  while ((1 << lrb) < rb) ++lrb;
   dim3 grid((a.H + rb - 1) / rb, a.n);
-  hipLaunchKernelGGL((down_kernel<FMT, G, NQ>), grid, dim3(kThreads), 0, s, ka, rb);
+  hipLaunchKernelGGL((down_kernel<FMT, G, NQ>), grid, dim3(kThreads), 0, s, ka, lrb);
   return hipGetLastError();
 }
 
@@ -451,7 +506,7 @@ hipError_t launch_down_g(const KArgs &ka, hipStream_t s) {
 template <int FMT>
 hipError_t launch_fmt(const KArgs &ka, hipStream_t s) {
   hipError_t e;
-  switch (pick_group(ka.gu.C)) {
+  switch (pick_group_gu(ka.gu.C)) {
     case 64: e = launch_gate_up_g<FMT, 64>(ka, s); break;
     case 32: e = launch_gate_up_g<FMT, 32>(ka, s); break;
     case 16: e = launch_gate_up_g<FMT, 16>(ka, s); break;
@@ -459,7 +514,7 @@ hipError_t launch_fmt(const KArgs &ka, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  switch (pick_group(ka.dn.C)) {
+  switch (pick_group_dn(ka.dn.C, ka.f.k)) {
     case 64: return launch_down_g<FMT, 64>(ka, s);
     case 32: return launch_down_g<FMT, 32>(ka, s);
     case 16: return launch_down_g<FMT, 16>(ka, s);
@@ -499,9 +554,8 @@ bool expert_ffn_supported(int format, int H, int I, int k) {
   const int epc = epc_of(format);
   if (!epc) return false;
   if (H % epc || I % epc) return false;
-  const int gu = pick_group(H / epc), dn = pick_group(I / epc);
-  if (!gu || !dn) return false;
-  if ((I / epc) / dn > 4) return false;  // down: at most 4 chunks per lane held in registers
+  const int gu = pick_group_gu(H / epc), dn = pick_group_dn(I / epc, k);
+  if (!gu || !dn) return false;  // down: at most 4 chunks per lane held in registers
   if (H > 16384) return false;          // x row staged in LDS by gate_up
   if (k > 32 || 16 * k > kMaxRed) return false;
   return true;

@@ -230,6 +230,7 @@ def test_route_logits_ties_and_order():
 # ------------------------------------------------------------------ FFN
 FFN_CASES = [
     ("bf16", 256, 128, 16, 2, 1), ("bf16", 256, 128, 16, 2, 4), ("bf16", 384, 192, 12, 3, 5),
+    ("bf16", 512, 512, 8, 4, 3), ("bf16", 1024, 256, 10, 6, 2),
     ("bf16", 2048, 768, 8, 8, 1), ("fp8_block128", 256, 256, 8, 2, 3), ("fp8_block128", 512, 256, 9, 4, 2),
     ("nvfp4", 256, 256, 8, 2, 3), ("nvfp4", 512, 256, 7, 4, 2), ("nvfp4", 7168, 256, 4, 2, 1),
 ]
@@ -269,3 +270,41 @@ def test_expert_ffn_matches_oracle(fmt, H, I, E, k, n):
     assert err <= tol
     # a tighter bound than the contract: bf16 output rounding plus bf16 intermediate
     assert err <= 5e-3
+
+
+def test_ffn_gated_off_after_failed_step():
+    """A failed ensure_experts turns the same step's FFN into a no-op (y untouched);
+    the next good step turns it back on."""
+    fmt, H, I, E, k, n = "bf16", 1024, 512, 8, 4, 2
+    _case("ffn gated by a failed step")
+    banks = {0: G.make_banks(fmt, E, H, I, tag="gate")}
+    c = G.make_cache(fmt, 1, E, H, I, E, banks)
+    c.load_rows(list(range(E)), list(range(E)))
+    c.set_state(np.arange(E, dtype=np.int64), np.zeros(E, np.uint64), 0)
+    host = G.oracle_host(banks, 1, 2)
+    rng = np.random.default_rng(1)
+    slot_ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(n)]).astype(np.int32)
+    w = np.full((n, k), 1.0 / k, dtype=np.float32)
+    x = synth.activations(n, H, 0, "gate").to(G.dev())
+    d_slots = torch.from_numpy(slot_ids).to(G.dev())
+    d_w = torch.from_numpy(w).to(G.dev())
+    ws = torch.empty(c.ffn_workspace_bytes(n, k), dtype=torch.uint8, device=G.dev())
+    ref = offn.expert_ffn(fmt, H, I, G.bits16(x), slot_ids, w.astype(np.float64),
+                          lambda s: [host[b][0][s] for b in range(2)])
+    y0, y1, y2 = [torch.empty((n, H), dtype=torch.int16, device=G.dev()) for _ in range(3)]
+    c.expert_ffn(x, d_slots, d_w, y0, ws)
+    bad = torch.tensor([[E + 3]], dtype=torch.int32, device=G.dev())
+    c.ensure_experts(0, bad, torch.empty_like(bad))
+    y1.fill_(7)
+    c.expert_ffn(x, d_slots, d_w, y1, ws)
+    torch.cuda.synchronize()
+    assert c.check_status() == oes.ERR_ARG
+    assert bool((y1 == 7).all())
+    ok_ids = torch.tensor([[0, 1]], dtype=torch.int32, device=G.dev())
+    c.ensure_experts(0, ok_ids, torch.empty_like(ok_ids))
+    c.expert_ffn(x, d_slots, d_w, y2, ws)
+    torch.cuda.synchronize()
+    c.check()
+    for y in (y0, y2):
+        assert offn.rel_l2(G.bf16_tensor_to_f64(y), ref) <= 5e-3
+    assert torch.equal(y0, y2)
