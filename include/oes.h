@@ -215,12 +215,13 @@ oes_status oes_route_workspace(int32_t n, int32_t hidden, int32_t num_experts, i
  *   ids [n, k] int32 device out, w [n, k] float device out
  *   logits [n, E] float device out, or NULL
  *   workspace: device, >= oes_route_workspace bytes, 16-byte aligned.
- * Limits: 1 <= k <= min(E, 32), E even and <= 512, n >= 0. */
+ * Limits: 1 <= k <= min(E, 32), E a multiple of 8 and <= 512, n >= 0. */
 oes_status oes_route(const void *x, const void *wg, int32_t n, int32_t hidden,
                      int32_t num_experts, int32_t k, int32_t *ids, float *w, float *logits,
                      void *workspace, int64_t workspace_bytes, void *stream);
 
-/* Top-k of given router logits [n, E] float device (prefill routes given logits). */
+/* Top-k of given router logits [n, E] float device (prefill routes given logits).
+ * Limits: 1 <= E <= 512, 1 <= k <= min(E, 32). */
 oes_status oes_route_logits(const float *logits, int32_t n, int32_t num_experts, int32_t k,
                             int32_t *ids, float *w, void *stream);
 

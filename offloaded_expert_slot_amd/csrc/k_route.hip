@@ -3,15 +3,17 @@
 // The pages name the top-k of each MoE layer (FreeToken MoE benchmark guide §4.3
 // routes bs * topk experts per step) but not the router; this is the plain one.
 //
-// Two launches:
+// Two launches, each one memory round trip deep:
 //   route_partial  - split-K GEMV: workgroup s sums rows [s*R, (s+1)*R) of
 //                    Wg [H, E] (bf16, row-major) against every token, fp32,
-//                    writing partial[s][t][e]; each thread owns one column pair
-//                    (a 4-byte load per row, coalesced along E).
-//   route_finish   - one wave per token: sums the (at most 32) partials in split
-//                    order (deterministic), writes the logits, picks the top-k
-//                    by repeated wave argmax (larger logit first, lower index on
-//                    ties) and the softmax over the chosen logits.
+//                    writing partial[s][t][e]; each thread owns one column octet
+//                    (a 16-byte load per row, coalesced along E) and up to 16
+//                    rows whose loads are all issued before the first multiply.
+//   route_finish   - one workgroup per token: all threads sum the partials
+//                    (deterministic order), then one wave writes the logits,
+//                    picks the top-k by repeated wave argmax (larger logit
+//                    first, lower index on ties) and the softmax over the
+//                    chosen logits.
 // route_logits runs route_finish alone on given logits (one split).
 
 #include <math.h>
@@ -25,56 +27,89 @@ namespace oes {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kTokBatch = 8;
+constexpr int kRpt = 16;        // rows per thread, all loads issued at once
+constexpr int kMaxTok = 32;     // tokens per pass of the partial kernel
 
-__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ inline float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-__global__ __launch_bounds__(kRouteThreads) void route_partial_kernel(const uint16_t *x, const uint32_t *wg2, int n,
-                                                                      int H, int E, int rows_per_split,
-                                                                      float *partial) {
-  __shared__ float red[kRouteThreads * 2 * kTokBatch];
-  const int cpt = E >> 1;                      // column pairs
-  const int rpp = kRouteThreads / cpt;         // rows processed in parallel
-  const int sub = threadIdx.x / cpt, cp = threadIdx.x % cpt;
+struct RouteGeom {
+  int cpt;    // column octets per row (E / 8)
+  int rpp;    // rows processed in parallel by a workgroup
+  int rows;   // rows per split (rpp * rows per thread)
+  int splits;
+};
+
+RouteGeom route_geom(int H, int E) {
+  RouteGeom g;
+  g.cpt = E / 8;
+  g.rpp = std::max(1, kRouteThreads / g.cpt);
+  // rows per thread: at most kRpt, and at most 256 rows per split (the x tile in LDS)
+  const int rpt = std::max(1, std::min(std::min(kRpt, 256 / g.rpp), (H + g.rpp - 1) / g.rpp));
+  g.rows = g.rpp * rpt;
+  g.splits = (H + g.rows - 1) / g.rows;
+  return g;
+}
+
+// Split-K GEMV: workgroup s owns rows [s*rows, (s+1)*rows) of Wg [H, E].  Thread
+// (sub, co) owns column octet co (one 16-byte load per row) and rows sub, sub +
+// rpp, ...; it issues every row load before the first multiply.  The x values
+// of the workgroup's rows are staged in LDS once.
+__global__ __launch_bounds__(kRouteThreads) void route_partial_kernel(const uint16_t *x, const uint16_t *wg, int n,
+                                                                      int H, int E, RouteGeom geo, float *partial) {
+  __shared__ float xs[kMaxTok * 256];    // [tok][row-in-split], rows <= 256
+  __shared__ float red[kRouteThreads * 8];
+  const int cpt = geo.cpt, rpp = geo.rpp;
+  const int sub = threadIdx.x / cpt, co = threadIdx.x % cpt;
   const bool active = sub < rpp;
-  const int r0 = blockIdx.x * rows_per_split;
-  const int r1 = min(H, r0 + rows_per_split);
-  for (int t0 = 0; t0 < n; t0 += kTokBatch) {
-    const int tn = min(kTokBatch, n - t0);
-    float acc[kTokBatch][2];
+  const int r0 = blockIdx.x * geo.rows;
+  const int nrows = min(geo.rows, H - r0);
+  u32x4 wv[kRpt];
 #pragma unroll
-    for (int t = 0; t < kTokBatch; ++t) acc[t][0] = acc[t][1] = 0.f;
-    if (active) {
-      for (int r = r0 + sub; r < r1; r += rpp) {
-        const uint32_t wv = wg2[(int64_t)r * cpt + cp];
-        const float w0 = bf16_lo(wv), w1 = bf16_hi(wv);
+  for (int i = 0; i < kRpt; ++i) {
+    const int rl = sub + i * rpp;
+    if (active && rl < nrows) wv[i] = *reinterpret_cast<const u32x4 *>(wg + (int64_t)(r0 + rl) * E + co * 8);
+  }
+  for (int t0 = 0; t0 < n; t0 += kMaxTok) {
+    const int tn = min(kMaxTok, n - t0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < tn * nrows; i += kRouteThreads) {
+      const int t = i / nrows, rl = i % nrows;
+      xs[t * 256 + rl] = bf16f(x[(int64_t)(t0 + t) * H + r0 + rl]);
+    }
+    __syncthreads();
+    for (int t = 0; t < tn; ++t) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (active) {
 #pragma unroll
-        for (int t = 0; t < kTokBatch; ++t) {
-          if (t < tn) {
-            const float xv = bf16f(x[(int64_t)(t0 + t) * H + r]);
-            acc[t][0] = fmaf(xv, w0, acc[t][0]);
-            acc[t][1] = fmaf(xv, w1, acc[t][1]);
+        for (int i = 0; i < kRpt; ++i) {
+          const int rl = sub + i * rpp;
+          if (rl < nrows) {
+            const float xv = xs[t * 256 + rl];
+            const u32x4 w = wv[i];
+            acc[0] = fmaf(xv, __uint_as_float(w.x << 16), acc[0]);
+            acc[1] = fmaf(xv, __uint_as_float(w.x & 0xffff0000u), acc[1]);
+            acc[2] = fmaf(xv, __uint_as_float(w.y << 16), acc[2]);
+            acc[3] = fmaf(xv, __uint_as_float(w.y & 0xffff0000u), acc[3]);
+            acc[4] = fmaf(xv, __uint_as_float(w.z << 16), acc[4]);
+            acc[5] = fmaf(xv, __uint_as_float(w.z & 0xffff0000u), acc[5]);
+            acc[6] = fmaf(xv, __uint_as_float(w.w << 16), acc[6]);
+            acc[7] = fmaf(xv, __uint_as_float(w.w & 0xffff0000u), acc[7]);
           }
         }
       }
-    }
-    // reduce the rpp row groups through LDS, in fixed order
-    __syncthreads();
-    if (active) {
+      // reduce the rpp row groups through LDS, in fixed order
+      if (active)
 #pragma unroll
-      for (int t = 0; t < kTokBatch; ++t) {
-        red[(sub * kTokBatch + t) * E + 2 * cp] = acc[t][0];
-        red[(sub * kTokBatch + t) * E + 2 * cp + 1] = acc[t][1];
+        for (int c = 0; c < 8; ++c) red[sub * E + co * 8 + c] = acc[c];
+      __syncthreads();
+      for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+        float s = 0.f;
+        for (int g = 0; g < rpp; ++g) s += red[g * E + e];
+        partial[((int64_t)blockIdx.x * n + t0 + t) * E + e] = s;
       }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < tn * E; idx += kRouteThreads) {
-      const int t = idx / E, e = idx % E;
-      float s = 0.f;
-      for (int g = 0; g < rpp; ++g) s += red[(g * kTokBatch + t) * E + e];
-      partial[((int64_t)blockIdx.x * n + t0 + t) * E + e] = s;
+      __syncthreads();
     }
   }
 }
@@ -90,36 +125,68 @@ __device__ inline bool better(const Cand &a, const Cand &b) {  // a ranks before
 
 constexpr int kMaxPerLane = 8;  // E <= 512 experts over 64 lanes
 
-// One wave per token: lane l owns experts l, l + 64, ...; the split partials are
-// summed in split order (deterministic), then k rounds of a wave-wide argmax
-// (larger logit first, lower index on ties) pick the top-k; lane j keeps the
-// j-th pick and writes its id and renormalised weight.
+// One workgroup per token.  All 256 threads sum the split partials (thread i
+// takes expert i % E and splits i / E, i / E + 256 / E, ... with independent
+// loads; the per-thread sums are added in a fixed order through LDS, so the
+// result is deterministic).  Then wave 0 picks the top-k by k rounds of a wave
+// argmax (larger logit first, lower index on ties); lane j keeps the j-th pick
+// and writes its id and renormalised weight.
 __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float *partial, int splits, int n, int E,
                                                                      int k, float *logits, int32_t *ids, float *w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
-  if (t >= n) return;
+  __shared__ float zsum[kRouteThreads];
+  __shared__ float z[512];
+  const int t = blockIdx.x;
   const int64_t stride = (int64_t)n * E;
-  float z[kMaxPerLane];
+  const int per = kRouteThreads / E >= 1 ? kRouteThreads / E : 1;   // threads per expert (E <= 256)
+  if (E <= kRouteThreads) {
+    const int e = threadIdx.x % E, part = threadIdx.x / E;
+    float s = 0.f;
+    if (part < per) {
+      const float *p = partial + (int64_t)t * E + e;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+      int sp = part;
+      for (; sp + 3 * per < splits; sp += 4 * per) {
+        a4[0] += p[(sp + 0 * per) * stride];
+        a4[1] += p[(sp + 1 * per) * stride];
+        a4[2] += p[(sp + 2 * per) * stride];
+        a4[3] += p[(sp + 3 * per) * stride];
+      }
+      for (; sp < splits; sp += per) a4[0] += p[sp * stride];
+      s = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    }
+    zsum[threadIdx.x] = s;
+    __syncthreads();
+    if (threadIdx.x < E) {
+      float tot = 0.f;
+      for (int q = 0; q < per; ++q) tot += zsum[q * E + threadIdx.x];
+      z[threadIdx.x] = tot;
+      if (logits) logits[(int64_t)t * E + threadIdx.x] = tot;
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+      const float *p = partial + (int64_t)t * E + e;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+      int sp = 0;
+      for (; sp + 4 <= splits; sp += 4) {
+        a4[0] += p[(sp + 0) * stride];
+        a4[1] += p[(sp + 1) * stride];
+        a4[2] += p[(sp + 2) * stride];
+        a4[3] += p[(sp + 3) * stride];
+      }
+      for (; sp < splits; ++sp) a4[0] += p[sp * stride];
+      const float tot = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+      z[e] = tot;
+      if (logits) logits[(int64_t)t * E + e] = tot;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  float zl[kMaxPerLane];
 #pragma unroll
   for (int q = 0; q < kMaxPerLane; ++q) {
     const int e = lane + 64 * q;
-    float s = 0.f;
-    if (e < E) {
-      const float *p = partial + (int64_t)t * E + e;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      int sp = 0;
-      for (; sp + 4 <= splits; sp += 4) {
-        a0 += p[(sp + 0) * stride];
-        a1 += p[(sp + 1) * stride];
-        a2 += p[(sp + 2) * stride];
-        a3 += p[(sp + 3) * stride];
-      }
-      for (; sp < splits; ++sp) a0 += p[sp * stride];
-      s = (a0 + a1) + (a2 + a3);
-      if (logits) logits[(int64_t)t * E + e] = s;
-    }
-    z[q] = s;
+    zl[q] = e < E ? z[e] : 0.f;
   }
   uint32_t taken = 0;
   float myv = 0.f;
@@ -130,7 +197,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float
     for (int q = 0; q < kMaxPerLane; ++q) {
       const int e = lane + 64 * q;
       if (e < E && !((taken >> q) & 1u)) {
-        Cand o{z[q], e};
+        Cand o{zl[q], e};
         if (c.i == 0x7fffffff || better(o, c)) c = o;
       }
     }
@@ -160,35 +227,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float
 
 }  // namespace
 
-int route_splits(int H, int E) {
-  const int rpp = kRouteThreads / (E / 2);
-  // at most 32 splits (the finishing wave sums them), each a multiple of rpp rows
-  int rows = std::max(rpp, (H + 31) / 32);
-  rows = (rows + rpp - 1) / rpp * rpp;
-  return (H + rows - 1) / rows;
-}
-
-static int route_rows_per_split(int H, int E) {
-  const int rpp = kRouteThreads / (E / 2);
-  int rows = std::max(rpp, (H + 31) / 32);
-  return (rows + rpp - 1) / rpp * rpp;
-}
+int route_splits(int H, int E) { return route_geom(H, E).splits; }
 
 hipError_t launch_route(const uint16_t *x, const uint16_t *wg, int n, int H, int E, int k, int32_t *ids, float *w,
                         float *logits, float *partial, hipStream_t s) {
-  const int splits = route_splits(H, E);
-  const int rows = route_rows_per_split(H, E);
-  hipLaunchKernelGGL(route_partial_kernel, dim3(splits), dim3(kRouteThreads), 0, s, x,
-                     reinterpret_cast<const uint32_t *>(wg), n, H, E, rows, partial);
+  const RouteGeom geo = route_geom(H, E);
+  hipLaunchKernelGGL(route_partial_kernel, dim3(geo.splits), dim3(kRouteThreads), 0, s, x, wg, n, H, E, geo, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_finish_kernel, dim3((n + 3) / 4), dim3(kRouteThreads), 0, s, partial, splits, n, E, k, logits,
+  hipLaunchKernelGGL(route_finish_kernel, dim3(n), dim3(kRouteThreads), 0, s, partial, geo.splits, n, E, k, logits,
                      ids, w);
   return hipGetLastError();
 }
 
 hipError_t launch_route_logits(const float *logits, int n, int E, int k, int32_t *ids, float *w, hipStream_t s) {
-  hipLaunchKernelGGL(route_finish_kernel, dim3((n + 3) / 4), dim3(kRouteThreads), 0, s, logits, 1, n, E, k,
+  hipLaunchKernelGGL(route_finish_kernel, dim3(n), dim3(kRouteThreads), 0, s, logits, 1, n, E, k,
                      static_cast<float *>(nullptr), ids, w);
   return hipGetLastError();
 }

@@ -73,7 +73,7 @@ def test_null_and_range_errors_without_gpu(L):
     ws = ctypes.c_int64()
     assert L.oes_route_workspace(4, 2048, 128, ctypes.byref(ws)) == oes.OK and ws.value > 0
     # route argument checks happen before any GPU work
-    assert L.oes_route(None, None, 1, 64, 7, 2, None, None, None, None, 0, None) == oes.ERR_ARG   # odd E
+    assert L.oes_route(None, None, 1, 64, 12, 2, None, None, None, None, 0, None) == oes.ERR_ARG  # E not a multiple of 8
     assert L.oes_route(None, None, 1, 64, 16, 0, None, None, None, None, 0, None) == oes.ERR_ARG  # k = 0
     assert L.oes_route(None, None, 1, 64, 16, 17, None, None, None, None, 0, None) == oes.ERR_ARG  # k > E
     assert L.oes_route(None, None, 0, 64, 16, 2, None, None, None, None, 0, None) == oes.OK       # empty
