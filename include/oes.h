@@ -306,11 +306,18 @@ oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x, const int
  * oes_probe_h2d_dma: one hipMemcpyAsync of `bytes` from pinned host to device.
  * oes_probe_h2d_kernel: the gather kernel's read of `bytes` of mapped pinned
  *   host memory into device memory (the zero-copy path's ceiling).
- * oes_probe_hbm_read: a streaming read of `bytes` of device memory. */
+ * oes_probe_hbm_read: a streaming read of `bytes` of device memory.
+ * oes_probe_mfma_bf16: `blocks` workgroups of 4 waves, each wave `iters` rounds of
+ *   8 independent v_mfma_f32_16x16x32_bf16 (the prefill GEMM's instruction) on
+ *   register operands; `*flops` receives the dense flops issued.  `sink` is a
+ *   device float the kernel may write (it never does in practice).  blocks >= 1,
+ *   1 <= iters <= 1 << 24. */
 oes_status oes_probe_h2d_dma(void *dev, const void *host, int64_t bytes, void *stream, float *ms);
 oes_status oes_probe_h2d_kernel(void *dev, const void *host, int64_t bytes, int32_t blocks,
                                 void *stream, float *ms);
 oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, void *sink, void *stream, float *ms);
+oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
+                               double *flops);
 
 /* ------------------------------------------------------------------ decoder check */
 /* Decode `n` elements of type `elem` (OES_ELEM_E4M3, OES_ELEM_FP4X2,

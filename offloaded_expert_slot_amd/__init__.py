@@ -109,6 +109,7 @@ _SIGS = {
     "oes_probe_h2d_dma": (_I32, [_P, _P, _I64, _P, _PF]),
     "oes_probe_h2d_kernel": (_I32, [_P, _P, _I64, _I32, _P, _PF]),
     "oes_probe_hbm_read": (_I32, [_P, _I64, _P, _P, _PF]),
+    "oes_probe_mfma_bf16": (_I32, [_I32, _I32, _P, _P, _PF, ctypes.POINTER(ctypes.c_double)]),
     "oes_debug_decode": (_I32, [_I32, _P, _I32, _P, _P]),
 }
 
@@ -381,3 +382,10 @@ def probe_hbm_read(dev, nbytes, sink, stream=None):
     ms = ctypes.c_float()
     _check(lib().oes_probe_hbm_read(_ptr(dev), nbytes, _ptr(sink), _stream(stream), ctypes.byref(ms)))
     return ms.value
+
+
+def probe_mfma_bf16(blocks, iters, sink, stream=None):
+    """(ms, flops) of the bf16 MFMA loop: blocks x 4 waves x iters x 8 MFMAs."""
+    ms, flops = ctypes.c_float(), ctypes.c_double()
+    _check(lib().oes_probe_mfma_bf16(blocks, iters, _ptr(sink), _stream(stream), ctypes.byref(ms), ctypes.byref(flops)))
+    return ms.value, flops.value

@@ -1004,6 +1004,21 @@ extern "C" oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, void *s
   return timed(s, ms, e0, e1);
 }
 
+extern "C" oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
+                                          double *flops) {
+  if (blocks < 1 || iters < 1 || iters > (1 << 24) || !sink || !ms || !flops)
+    return fail(OES_ERR_ARG, "bad probe arguments");
+  hipStream_t s = as_stream(stream);
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  HIP_TRY(hipEventRecord(e0, s));
+  HIP_TRY(launch_mfma_probe(blocks, iters, static_cast<float *>(sink), s));
+  HIP_TRY(hipEventRecord(e1, s));
+  *flops = (double)mfma_probe_flops(blocks, iters);
+  return timed(s, ms, e0, e1);
+}
+
 extern "C" oes_status oes_debug_decode(int32_t elem, const void *codes, int32_t n, float *out, void *stream) {
   if (n < 0) return fail(OES_ERR_ARG, "n < 0");
   if (n == 0) return OES_OK;

@@ -19,15 +19,14 @@
 //
 // GEMM tiling (v_mfma_f32_16x16x32_bf16; lane l holds A[l%16][8(l/16)..+7],
 // B[8(l/16)..+7][l%16], D[4(l/16)+r][l%16]):
-//   block = (expert, 64 output features) x all rows of the expert in passes of
-//   128; wave w owns 16 features (gate_up: those 16 gate rows and the matching
-//   16 up rows, so silu(g) * u is formed in registers).  K runs in steps of 64
-//   (two 32-element MXFP4 blocks).  The A tile (128 rows x 64 k, bf16) is
-//   double-buffered in LDS; the B operand needs no LDS: for a 32-element block
-//   kb and row n the K-block-major layout [K/32][N][16 B] puts the 8 codes lane l
-//   needs in dword l/16 of the 16 bytes at (kb, n), so one dword load per lane
-//   (a contiguous 256 B per wave) feeds one MFMA after four fp4 -> bf16 scaled
-//   conversions (exact: e2m1 * 2^k is a bf16 number).
+//   block = (expert, 64 / 128 output features) x all rows of the expert in
+//   passes of 96; in gate_up, wave w owns 16 features (those 16 gate rows and
+//   the matching 16 up rows, so silu(g) * u is formed in registers).  K runs in
+//   quads of four 32-element MXFP4 blocks.  The A chunk of a quad is staged in
+//   LDS from registers loaded one quad ahead; the B operand needs no LDS: the
+//   K-block-major layout [K/32][N][16 B] gives each lane one 16-byte load per
+//   quad that feeds four MFMAs after fp4 -> bf16 scaled conversions (exact:
+//   e2m1 * 2^k is a bf16 number).
 //   Blocks are mapped XCD-aware: hardware deals consecutive block indices to
 //   the 8 XCDs in turn, so block b runs on XCD b % 8; experts e with e % 8 == x
 //   are given to XCD x, which keeps an expert's activation rows in one L2
@@ -50,12 +49,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int BM = 128;            // rows per pass
-constexpr int MT = BM / 16;        // m-tiles per pass
-constexpr int BKS = 64;            // k per step: two MXFP4 blocks
-constexpr int NF = 64;             // output features per block: 4 waves x 16
-constexpr int LDA = BKS + 8;       // padded LDS row, bf16 elements (144 B: spreads banks)
+constexpr int BM = 96;             // rows per pass: six 16-row m-tiles
+constexpr int LDA = 128 + 8;       // LDS row of one 128-k quad, bf16 elements, padded 16 B
 constexpr int kXcds = 8;
+static_assert(kThreads == 256, "an A piece per thread covers one row of each m-tile");
 
 struct GemmArgs {
   int32_t H, I, E, k, nk;
@@ -124,151 +121,251 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int n
 }
 
 // ------------------------------------------------------------------ grouped GEMM
+// Block = (expert, feature tile), 4 waves; rows of the expert in passes of at
+// most BM, each pass run by a body specialised on its m-tile count so that its
+// quad loop has no branches.
+//
+// K order inside a quad.  K runs in quads of four 32-element MXFP4 blocks (128
+// k).  An MFMA sums over its 32 k-slots in any order as long as A and B use the
+// same one, so in MFMA step j (0..3) of a quad starting at block kb0, lane group
+// lq = l/16 feeds k-slots 8lq..8lq+7 with the real k = 32(kb0 + lq) + 8j + i.
+// Lane (l16, lq) then needs all 32 codes of block kb0 + lq of its row, which are
+// the 16 contiguous bytes at (kb0 + lq, row) of the [K/32][N][16] bank: one
+// 16-byte load per lane feeds four MFMAs, and its one scale byte covers them.
+//
+// Pipelining.  B: each wave keeps a ring of KRING quads per n-tile in registers;
+// the slot of quad q is converted to bf16 and at once refilled with quad
+// q + KRING.  A: the chunk of quad q + 1 (16 rows per m-tile x 128 k, bf16) is
+// loaded into registers while quad q is multiplied from LDS, then stored to the
+// other LDS buffer; one barrier per quad.  Each output row of an MFMA depends
+// only on its own A row, so A rows past the pass's last row are left as they are
+// (their outputs are never stored); k past K is zero, against clamped B blocks.
+//
+// Each wave owns two 16-feature n-tiles: gate_up - the gate tile and the up tile
+// of the same 16 features (64 features per block); down - two consecutive tiles
+// (128 features per block; tiles past the last feature are computed on clamped
+// rows and not stored).
+constexpr int KRING = 3;
+constexpr int NTW = 2;
+
+struct Tile {
+  int e, off, m0, mrows;
+  int K, N, nkb, nq;
+  int nrow[NTW], f[NTW];
+  bool tile_on[NTW];
+  int l16, lq;
+};
+
+template <int PHASE, int MTS>
+__device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint16_t (*As)[BM * LDA],
+                                          const int64_t *rowoff) {
+  const uint8_t *blk = g.blocks + (int64_t)T.e * g.blocks_stride;
+  const uint8_t *scl = g.scales + (int64_t)T.e * g.scales_stride;
+  const uint16_t *asrc = PHASE == 0 ? g.x : g.hbuf;
+  const int l16 = T.l16, lq = T.lq;
+  const int c16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;  // A piece: row rsub of each m-tile
+
+  f32x4 acc[MTS][NTW];
+#pragma unroll
+  for (int i = 0; i < MTS; ++i)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int64_t aoff[MTS];
+#pragma unroll
+  for (int i = 0; i < MTS; ++i) aoff[i] = rowoff[16 * i + rsub];
+  u32x4 areg[MTS];
+  auto load_a = [&](int q) {
+    const int k0 = q * 128 + c16 * 8;
+#pragma unroll
+    for (int i = 0; i < MTS; ++i)
+      areg[i] = (aoff[i] >= 0 && k0 < T.K)
+                    ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(asrc + aoff[i] + k0))
+                    : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < MTS; ++i) *reinterpret_cast<u32x4 *>(&As[buf][(16 * i + rsub) * LDA + c16 * 8]) = areg[i];
+  };
+  // B ring: slot d holds quad q (q % KRING == d) for both n-tiles.  Blocks past
+  // K are clamped to the last one: the A k-slots they meet are zero.
+  u32x4 bw[KRING][NTW];
+  uint32_t bs[KRING][NTW];
+  auto load_b = [&](int d, int q) {
+    const int kb = min(4 * q + lq, T.nkb - 1);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const int64_t idx = (int64_t)kb * T.N + T.nrow[t];
+      bw[d][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(blk + idx * 16));
+      bs[d][t] = scl[idx];
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < KRING; ++d) load_b(d, d);
+  load_a(0);
+  store_a(0);
+  __syncthreads();
+  for (int q0 = 0; q0 < T.nq; q0 += KRING) {
+#pragma unroll
+    for (int d = 0; d < KRING; ++d) {
+      const int q = q0 + d;
+      if (q < T.nq) {
+        const bool more = q + 1 < T.nq;
+        if (more) load_a(q + 1);
+        bf16x8 bop[4][NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const float sc = e8m0f(bs[d][t]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bop[j][t] = fp4x8_bf16(bw[d][t][j], sc);
+        }
+        load_b(d, q + KRING);
+        const uint16_t *Ab = As[q & 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int mt = 0; mt < MTS; ++mt) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&Ab[(mt * 16 + l16) * LDA + lq * 32 + j * 8]);
+#pragma unroll
+            for (int t = 0; t < NTW; ++t)
+              acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[j][t], acc[mt][t], 0, 0, 0);
+          }
+        }
+        if (more) store_a((q + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue: acc[mt][t][r] is row mt*16 + 4*lq + r of the pass, feature f[t]
+  const uint16_t *bias = g.bias + (int64_t)T.e * g.bias_stride;
+  if (PHASE == 0) {
+    if (T.tile_on[0]) {
+      const float bg = bf16f(bias[T.f[0]]), bu = bf16f(bias[g.I + T.f[0]]);
+#pragma unroll
+      for (int mt = 0; mt < MTS; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mt * 16 + lq * 4 + r;
+          if (m < T.mrows) {
+            const float gv = acc[mt][0][r] + bg, uv = acc[mt][1][r] + bu;
+            const float hv = gv / (1.f + __expf(-gv)) * uv;
+            g.hbuf[(int64_t)(T.off + T.m0 + m) * g.I + T.f[0]] = to_bf16(hv);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      if (!T.tile_on[t]) continue;
+      const float bd = bf16f(bias[T.f[t]]);
+#pragma unroll
+      for (int mt = 0; mt < MTS; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mt * 16 + lq * 4 + r;
+          if (m < T.mrows) {
+            const int p = g.perm[T.off + T.m0 + m];
+            g.obuf[(int64_t)p * g.H + T.f[t]] = acc[mt][t][r] + bd;
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int PHASE>
-__global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
-  constexpr int NTW = PHASE == 0 ? 2 : 1;  // n-tiles per wave: (gate, up) or one down tile
+__global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
+  constexpr int NFB = PHASE == 0 ? 64 : 128;  // features per block
   __shared__ __align__(16) uint16_t As[2][BM * LDA];
-  int e, nt;
+  __shared__ int64_t rowoff[BM];
+  Tile T;
+  int nt;
   if (g.xcd) {
     const int x = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-    e = x + kXcds * (local / g.ntiles);
+    T.e = x + kXcds * (local / g.ntiles);
     nt = local % g.ntiles;
   } else {
-    e = blockIdx.x / g.ntiles;
+    T.e = blockIdx.x / g.ntiles;
     nt = blockIdx.x % g.ntiles;
   }
-  if (e >= g.E) return;
-  const int off = g.offsets[e];
-  const int m_e = g.offsets[e + 1] - off;
+  if (T.e >= g.E) return;
+  T.off = g.offsets[T.e];
+  const int m_e = g.offsets[T.e + 1] - T.off;
   if (m_e <= 0) return;
-  const int K = PHASE == 0 ? g.H : g.I;    // reduction length
-  const int N = PHASE == 0 ? 2 * g.I : g.H;  // weight rows of the matrix
-  const int ksteps = K / BKS;
+  T.K = PHASE == 0 ? g.H : g.I;
+  T.N = PHASE == 0 ? 2 * g.I : g.H;
+  const int nfeat = PHASE == 0 ? g.I : g.H;
+  T.nkb = T.K / 32;
+  T.nq = (T.nkb + 3) >> 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int l16 = lane & 15, lq = lane >> 4;
-  const int f0 = nt * NF + wave * 16;      // first feature of this wave
-  int nrow[NTW];
-  nrow[0] = f0 + l16;
-  if (NTW == 2) nrow[NTW - 1] = g.I + f0 + l16;  // up row of the same feature
-  const uint8_t *blk = g.blocks + (int64_t)e * g.blocks_stride;
-  const uint8_t *scl = g.scales + (int64_t)e * g.scales_stride;
-  const uint16_t *bias = g.bias + (int64_t)e * g.bias_stride;
-
-  // A-tile loader: thread t moves row t/2, k half (t%2)*32 of the step: 4 x 16 B
-  const int arow = threadIdx.x >> 1, akh = (threadIdx.x & 1) * 32;
-
-  for (int m0 = 0; m0 < m_e; m0 += BM) {
-    const int mrows = min(BM, m_e - m0);
-    const int mtiles = (mrows + 15) >> 4;
-    const uint16_t *asrc = nullptr;
-    if (arow < mrows) {
-      if (PHASE == 0)
-        asrc = g.x + (int64_t)(g.perm[off + m0 + arow] / g.k) * g.H + akh;
-      else
-        asrc = g.hbuf + (int64_t)(off + m0 + arow) * g.I + akh;
-    }
-    f32x4 acc[MT][NTW];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 areg[4];
-    uint32_t bw[NTW][2], bs[NTW][2];
-    auto load_a = [&](int s) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        areg[q] = asrc ? *reinterpret_cast<const u32x4 *>(asrc + s * BKS + q * 8) : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto store_a = [&](int buf) {
-      u32x4 *d = reinterpret_cast<u32x4 *>(&As[buf][arow * LDA + akh]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = areg[q];
-    };
-    auto load_b = [&](int s) {
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kb = 2 * s + h;
-          bw[j][h] = *reinterpret_cast<const uint32_t *>(blk + ((int64_t)kb * N + nrow[j]) * 16 + 4 * lq);
-          bs[j][h] = scl[(int64_t)kb * N + nrow[j]];
-        }
-    };
-
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    __syncthreads();
-    for (int s = 0; s < ksteps; ++s) {
-      const int cur = s & 1;
-      uint32_t cw[NTW][2], cs[NTW][2];
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          cw[j][h] = bw[j][h];
-          cs[j][h] = bs[j][h];
-        }
-      if (s + 1 < ksteps) {
-        load_a(s + 1);
-        load_b(s + 1);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 bop[NTW];
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) bop[j] = fp4x8_bf16(cw[j][h], e8m0f(cs[j][h]));
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          if (i < mtiles) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8 *>(&As[cur][(i * 16 + l16) * LDA + h * 32 + lq * 8]);
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[j], acc[i][j], 0, 0, 0);
-          }
-        }
-      }
-      if (s + 1 < ksteps) store_a(cur ^ 1);
-      __syncthreads();
-    }
-
-    // epilogue: rows 4*lq + r of each m-tile, feature f0 + l16
-    const int f = f0 + l16;
-    if (PHASE == 0) {
-      const float bg = bf16f(bias[f]), bu = bf16f(bias[g.I + f]);
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        if (i < mtiles) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + lq * 4 + r;
-            if (m < mrows) {
-              const float gv = acc[i][0][r] + bg, uv = acc[i][NTW - 1][r] + bu;
-              const float hv = gv / (1.f + __expf(-gv)) * uv;
-              g.hbuf[(int64_t)(off + m0 + m) * g.I + f] = to_bf16(hv);
-            }
-          }
-        }
-      }
-    } else {
-      const float bd = bf16f(bias[f]);
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        if (i < mtiles) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + lq * 4 + r;
-            if (m < mrows) {
-              const int p = g.perm[off + m0 + m];
-              g.obuf[(int64_t)p * g.H + f] = acc[i][0][r] + bd;
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();  // the next pass reuses the LDS tiles
+  T.l16 = lane & 15;
+  T.lq = lane >> 4;
+  const int fbase = nt * NFB + wave * (PHASE == 0 ? 16 : 32);
+  if (PHASE == 0) {
+    T.f[0] = T.f[1] = fbase + T.l16;
+    T.nrow[0] = min(T.f[0], g.I - 1);
+    T.nrow[1] = g.I + T.nrow[0];
+    T.tile_on[0] = T.tile_on[1] = fbase < nfeat;
+  } else {
+    T.f[0] = fbase + T.l16;
+    T.f[1] = T.f[0] + 16;
+    T.nrow[0] = min(T.f[0], T.N - 1);
+    T.nrow[1] = min(T.f[1], T.N - 1);
+    T.tile_on[0] = fbase < nfeat;
+    T.tile_on[1] = fbase + 16 < nfeat;
   }
+  const int lda_src = PHASE == 0 ? g.H : g.I;
+
+  for (T.m0 = 0; T.m0 < m_e; T.m0 += BM) {
+    T.mrows = min(BM, m_e - T.m0);
+    __syncthreads();  // the previous pass is done with rowoff and As
+    for (int r = threadIdx.x; r < BM; r += kThreads) {
+      int64_t o = -1;
+      if (r < T.mrows) {
+        const int64_t src_row =
+            PHASE == 0 ? (int64_t)(g.perm[T.off + T.m0 + r] / g.k) : (int64_t)(T.off + T.m0 + r);
+        o = src_row * lda_src;
+      }
+      rowoff[r] = o;
+    }
+    __syncthreads();
+    switch ((T.mrows + 15) >> 4) {
+      case 1: gemm_pass<PHASE, 1>(g, T, As, rowoff); break;
+      case 2: gemm_pass<PHASE, 2>(g, T, As, rowoff); break;
+      case 3: gemm_pass<PHASE, 3>(g, T, As, rowoff); break;
+      case 4: gemm_pass<PHASE, 4>(g, T, As, rowoff); break;
+      case 5: gemm_pass<PHASE, 5>(g, T, As, rowoff); break;
+      default: gemm_pass<PHASE, 6>(g, T, As, rowoff); break;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MFMA ceiling
+// Eight independent accumulator chains of v_mfma_f32_16x16x32_bf16 per wave, the
+// instruction the grouped GEMM uses; operands stay in registers.  The result is
+// stored only on an impossible value, which keeps the chains live.
+__global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(lane + i));
+    b[i] = (__bf16)(0.002f * (float)(lane - i));
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{(float)c, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) t += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (t == 1234.5678f) sink[0] = t;
 }
 
 // ------------------------------------------------------------------ combine
@@ -314,6 +411,13 @@ WsLayout ws_layout(int H, int I, int n, int k, int E) {
 
 }  // namespace
 
+hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kThreads), 0, s, iters, sink);
+  return hipGetLastError();
+}
+
+int64_t mfma_probe_flops(int blocks, int iters) { return (int64_t)blocks * (kThreads / 64) * iters * 8 * 16 * 16 * 32 * 2; }
+
 bool prefill_supported(int H, int I, int E) { return H % 64 == 0 && I % 64 == 0 && E <= OES_MAX_EXPERTS; }
 
 int64_t prefill_workspace_bytes(int H, int I, int n, int k, int E) { return ws_layout(H, I, n, k, E).total; }
@@ -350,7 +454,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   g.blocks_stride = a.row_bytes[0];
   g.scales_stride = a.row_bytes[1];
   g.bias_stride = a.row_bytes[2] / 2;
-  g.ntiles = a.I / NF;
+  g.ntiles = (a.I + 63) / 64;
   hipLaunchKernelGGL(moe_gemm_kernel<0>, dim3(a.E * g.ntiles), dim3(kThreads), 0, s, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -361,7 +465,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   g.blocks_stride = a.row_bytes[3];
   g.scales_stride = a.row_bytes[4];
   g.bias_stride = a.row_bytes[5] / 2;
-  g.ntiles = a.H / NF;
+  g.ntiles = (a.H + 127) / 128;
   hipLaunchKernelGGL(moe_gemm_kernel<1>, dim3(a.E * g.ntiles), dim3(kThreads), 0, s, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

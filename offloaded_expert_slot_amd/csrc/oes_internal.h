@@ -104,6 +104,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_stream_copy(uint8_t *dst, const uint8_t *src, int64_t bytes, int blocks,
                               hipStream_t s);
 hipError_t launch_hbm_read(const uint8_t *src, int64_t bytes, float *sink, hipStream_t s);
+hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t s);
+int64_t mfma_probe_flops(int blocks, int iters);
 
 // ---------------------------------------------------------------- debug decode
 // out[i] = value of element i of `elem` codes (fp4x2: 2 per byte, element 2j low nibble)
