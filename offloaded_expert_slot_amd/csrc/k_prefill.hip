@@ -17,16 +17,15 @@
 //                pair's row.
 //   combine    - y_t = sum_j w[t, j] * o_{t,j} in pair order, bf16.
 //
-// GEMM tiling (v_mfma_f32_16x16x32_bf16; lane l holds A[l%16][8(l/16)..+7],
-// B[8(l/16)..+7][l%16], D[4(l/16)+r][l%16]):
-//   block = (expert, 64 / 128 output features) x all rows of the expert in
-//   passes of 96; in gate_up, wave w owns 16 features (those 16 gate rows and
-//   the matching 16 up rows, so silu(g) * u is formed in registers).  K runs in
+// GEMM tiling (v_mfma_f32_32x32x16_bf16, details at the kernel):
+//   block = (expert, 128 / 256 output features) x all rows of the expert in
+//   passes of 96; in gate_up, wave w owns 32 features (those 32 gate rows and
+//   the matching 32 up rows, so silu(g) * u is formed in registers).  K runs in
 //   quads of four 32-element MXFP4 blocks.  The A chunk of a quad is staged in
 //   LDS from registers loaded one quad ahead; the B operand needs no LDS: the
 //   K-block-major layout [K/32][N][16 B] gives each lane one 16-byte load per
-//   quad that feeds four MFMAs after fp4 -> bf16 scaled conversions (exact:
-//   e2m1 * 2^k is a bf16 number).
+//   pair of blocks that feeds four MFMAs after fp4 -> bf16 scaled conversions
+//   (exact: e2m1 * 2^k is a bf16 number).
 //   Blocks are mapped XCD-aware: hardware deals consecutive block indices to
 //   the 8 XCDs in turn, so block b runs on XCD b % 8; experts e with e % 8 == x
 //   are given to XCD x, which keeps an expert's activation rows in one L2
@@ -45,14 +44,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;  // a global-memory u32x4
 
 constexpr int kThreads = 256;
-constexpr int BM = 96;             // rows per pass: six 16-row m-tiles
+constexpr int BM = 96;             // rows per pass: three 32-row m-tiles
 constexpr int LDA = 128 + 8;       // LDS row of one 128-k quad, bf16 elements, padded 16 B
 constexpr int kXcds = 8;
-static_assert(kThreads == 256, "an A piece per thread covers one row of each m-tile");
+constexpr int kMaxKb = 96;         // K / 32 limit of the grouped GEMM (K <= 3072)
+static_assert(kThreads == 256, "two A pieces per thread cover one row of each half m-tile");
 
 struct GemmArgs {
   int32_t H, I, E, k, nk;
@@ -65,6 +67,7 @@ struct GemmArgs {
   const uint8_t *scales;   // this phase's _scales bank
   const uint16_t *bias;    // this phase's _bias bank (bf16)
   int64_t blocks_stride, scales_stride, bias_stride;
+  const u32x4 *zero16;   // 16 zero bytes: the source of A pieces past K
   uint16_t *hbuf;        // [nk, I] bf16, expert order
   float *obuf;           // [nk, H] fp32, pair order
 };
@@ -94,7 +97,8 @@ __device__ inline bf16x8 fp4x8_bf16(uint32_t v, float s) {
 
 // ------------------------------------------------------------------ permute
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int nk, int E, int32_t *offsets,
-                                                       int32_t *perm) {
+                                                       int32_t *perm, uint32_t *zeros) {
+  if (threadIdx.x < 64) zeros[threadIdx.x] = 0u;  // the GEMMs' 256-byte zero source
   __shared__ int hist[OES_MAX_EXPERTS];
   __shared__ int cursor[OES_MAX_EXPERTS];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
@@ -122,132 +126,161 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int n
 
 // ------------------------------------------------------------------ grouped GEMM
 // Block = (expert, feature tile), 4 waves; rows of the expert in passes of at
-// most BM, each pass run by a body specialised on its m-tile count so that its
-// quad loop has no branches.
+// most BM = 96, each pass run by a body specialised on its count of 32-row
+// m-tiles so that its quad loop has no branches.  v_mfma_f32_32x32x16_bf16:
+// lane l holds A[l%32][8(l/32)..+7] and B[8(l/32)..+7][l%32]; D element r of
+// lane l is row 4(l/32) + (r%4) + 8(r/4), column l%32.
 //
-// K order inside a quad.  K runs in quads of four 32-element MXFP4 blocks (128
-// k).  An MFMA sums over its 32 k-slots in any order as long as A and B use the
-// same one, so in MFMA step j (0..3) of a quad starting at block kb0, lane group
-// lq = l/16 feeds k-slots 8lq..8lq+7 with the real k = 32(kb0 + lq) + 8j + i.
-// Lane (l16, lq) then needs all 32 codes of block kb0 + lq of its row, which are
-// the 16 contiguous bytes at (kb0 + lq, row) of the [K/32][N][16] bank: one
-// 16-byte load per lane feeds four MFMAs, and its one scale byte covers them.
+// K order.  K runs in quads of four 32-element MXFP4 blocks (128 k), a quad in
+// two pairs.  An MFMA sums over its 16 k-slots in any order as long as A and B
+// use the same one, so in step j (0..3) of the pair starting at block kb0, lane
+// half h = l/32 feeds k-slots 8h..8h+7 with the real k = 32(kb0 + h) + 8j + i.
+// Lane (n, h) then needs all 32 codes of block kb0 + h of weight row n: the 16
+// contiguous bytes at (kb0 + h, n) of the [K/32][N][16] bank, one 16-byte load
+// per lane for four MFMAs, with one scale byte.
 //
-// Pipelining.  B: each wave keeps a ring of KRING quads per n-tile in registers;
-// the slot of quad q is converted to bf16 and at once refilled with quad
-// q + KRING.  A: the chunk of quad q + 1 (16 rows per m-tile x 128 k, bf16) is
-// loaded into registers while quad q is multiplied from LDS, then stored to the
-// other LDS buffer; one barrier per quad.  Each output row of an MFMA depends
-// only on its own A row, so A rows past the pass's last row are left as they are
-// (their outputs are never stored); k past K is zero, against clamped B blocks.
+// Pipelining.  The block's scale bytes (its 256 weight rows x K/32 blocks) are
+// copied to LDS once.  B: each wave holds one quad's two pairs per n-tile in
+// registers; pair p of quad q + 1 is loaded as soon as quad q's MFMA steps on
+// pair p are issued.  A: the chunk of quad q + 1 (the pass's rows x 128 k,
+// bf16) is loaded into registers while quad q is multiplied from LDS, then
+// stored to the other LDS buffer; one barrier per quad.  The steady-state loop
+// has no conditions, so the compiler's memory-counter waits stay exact.
+// Indexes past the data are clamped (B) or pointed at a zero block (A, k past
+// K), never branched on.  Each output row of an MFMA depends only on its own A
+// row, so A rows past the pass's last row may hold anything: their outputs are
+// never stored.
 //
-// Each wave owns two 16-feature n-tiles: gate_up - the gate tile and the up tile
-// of the same 16 features (64 features per block); down - two consecutive tiles
-// (128 features per block; tiles past the last feature are computed on clamped
-// rows and not stored).
-constexpr int KRING = 3;
+// Each wave owns two 32-feature n-tiles: gate_up - the gate tile and the up
+// tile of the same 32 features (128 features per block); down - two consecutive
+// tiles (256 features per block).  Tiles past the last feature run on clamped
+// rows and are not stored.
+constexpr int kUnroll = 2;  // quads per steady-state iteration: the LDS buffer parity is static
 constexpr int NTW = 2;
+constexpr int kRowsB = 256;  // weight rows per block
 
 struct Tile {
   int e, off, m0, mrows;
   int K, N, nkb, nq;
-  int nrow[NTW], f[NTW];
+  int nrow[NTW], f[NTW], lrow[NTW];
   bool tile_on[NTW];
-  int l16, lq;
+  int n32, h;
 };
 
-template <int PHASE, int MTS>
+// e8m0 byte -> fp32 2^(e-127): e << 23, with 0 -> 2^-127 (0x00400000) and
+// 255 -> NaN (0x7fc00000), both by setting bit 22; no branches
+__device__ __forceinline__ float e8m0_bits(uint32_t e) {
+  return __uint_as_float((e << 23) | ((uint32_t)(e == 0u || e == 255u) << 22));
+}
+
+template <int PHASE, int MT>
 __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint16_t (*As)[BM * LDA],
-                                          const int64_t *rowoff) {
+                                          const int32_t *rowoff, const uint8_t *sc_lds) {
+  constexpr int AP = 2 * MT;  // 16-byte A pieces per thread per quad
   const uint8_t *blk = g.blocks + (int64_t)T.e * g.blocks_stride;
-  const uint8_t *scl = g.scales + (int64_t)T.e * g.scales_stride;
   const uint16_t *asrc = PHASE == 0 ? g.x : g.hbuf;
-  const int l16 = T.l16, lq = T.lq;
-  const int c16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;  // A piece: row rsub of each m-tile
+  const int n32 = T.n32, h = T.h;
+  const int c16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;  // A piece: row 16i + rsub, column c16
 
-  f32x4 acc[MTS][NTW];
+  f32x16 acc[MT][NTW];
 #pragma unroll
-  for (int i = 0; i < MTS; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
 
-  int64_t aoff[MTS];
+  // A rows: rowoff < 0 marks a row past the pass (read row 0 instead)
+  int32_t aoff[AP];
 #pragma unroll
-  for (int i = 0; i < MTS; ++i) aoff[i] = rowoff[16 * i + rsub];
-  u32x4 areg[MTS];
+  for (int i = 0; i < AP; ++i) aoff[i] = max(rowoff[16 * i + rsub], 0);
+  // pieces past K read the zero block: a select on the loaded value would make
+  // the wave wait for the loads at once instead of at the quad's end
+  const uint64_t zero_addr = reinterpret_cast<uint64_t>(g.zero16);
+  u32x4 areg[AP];
   auto load_a = [&](int q) {
     const int k0 = q * 128 + c16 * 8;
+    const bool kin = k0 < T.K;
 #pragma unroll
-    for (int i = 0; i < MTS; ++i)
-      areg[i] = (aoff[i] >= 0 && k0 < T.K)
-                    ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(asrc + aoff[i] + k0))
-                    : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < AP; ++i) {
+      uint64_t src = kin ? reinterpret_cast<uint64_t>(asrc + aoff[i] + k0) : zero_addr;
+      asm volatile("" : "+v"(src));  // keep the select on the address
+      areg[i] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4 *>(src));
+    }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < MTS; ++i) *reinterpret_cast<u32x4 *>(&As[buf][(16 * i + rsub) * LDA + c16 * 8]) = areg[i];
+    for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4 *>(&As[buf][(16 * i + rsub) * LDA + c16 * 8]) = areg[i];
   };
-  // B ring: slot d holds quad q (q % KRING == d) for both n-tiles.  Blocks past
-  // K are clamped to the last one: the A k-slots they meet are zero.
-  u32x4 bw[KRING][NTW];
-  uint32_t bs[KRING][NTW];
-  auto load_b = [&](int d, int q) {
-    const int kb = min(4 * q + lq, T.nkb - 1);
+  // B: one quad's two pairs; pair p of quad q + 1 is loaded as soon as quad q's
+  // steps on pair p are issued
+  u32x4 bw[2][NTW];
+  const uint8_t *bptr[NTW];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const int64_t idx = (int64_t)kb * T.N + T.nrow[t];
-      bw[d][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(blk + idx * 16));
-      bs[d][t] = scl[idx];
-    }
+  for (int t = 0; t < NTW; ++t) bptr[t] = blk + (int64_t)T.nrow[t] * 16;
+  const int64_t kstride = (int64_t)T.N * 16;
+  auto load_bp = [&](int p, int q) {
+    const int kb = min(4 * q + 2 * p + h, T.nkb - 1);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+      bw[p][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(bptr[t] + kb * kstride));
   };
 
+  auto quad = [&](int q, bool more) {
+    if (more) load_a(q + 1);
+    const uint16_t *Ab = As[q & 1];
 #pragma unroll
-  for (int d = 0; d < KRING; ++d) load_b(d, d);
+    for (int p = 0; p < 2; ++p) {
+      const int kb = min(4 * q + 2 * p + h, T.nkb - 1);
+      float sc[NTW];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) sc[t] = e8m0_bits(sc_lds[kb * kRowsB + T.lrow[t]]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 bop[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) bop[t] = fp4x8_bf16(bw[p][t][j], sc[t]);
+        if (j == 3) load_bp(p, q + 1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 av =
+              *reinterpret_cast<const bf16x8 *>(&Ab[(mt * 32 + n32) * LDA + (2 * p + h) * 32 + j * 8]);
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+            acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bop[t], acc[mt][t], 0, 0, 0);
+        }
+      }
+    }
+    if (more) store_a((q + 1) & 1);
+    __syncthreads();
+  };
+
+  load_bp(0, 0);
+  load_bp(1, 0);
   load_a(0);
   store_a(0);
   __syncthreads();
-  for (int q0 = 0; q0 < T.nq; q0 += KRING) {
+  // steady state: every quad of the group has a successor
+  int q0 = 0;
+  for (; q0 + kUnroll < T.nq; q0 += kUnroll) {
 #pragma unroll
-    for (int d = 0; d < KRING; ++d) {
-      const int q = q0 + d;
-      if (q < T.nq) {
-        const bool more = q + 1 < T.nq;
-        if (more) load_a(q + 1);
-        bf16x8 bop[4][NTW];
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-          const float sc = e8m0f(bs[d][t]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bop[j][t] = fp4x8_bf16(bw[d][t][j], sc);
-        }
-        load_b(d, q + KRING);
-        const uint16_t *Ab = As[q & 1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int mt = 0; mt < MTS; ++mt) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&Ab[(mt * 16 + l16) * LDA + lq * 32 + j * 8]);
-#pragma unroll
-            for (int t = 0; t < NTW; ++t)
-              acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[j][t], acc[mt][t], 0, 0, 0);
-          }
-        }
-        if (more) store_a((q + 1) & 1);
-        __syncthreads();
-      }
-    }
+    for (int d = 0; d < kUnroll; ++d) quad(q0 + d, true);
   }
+  // the last one to kUnroll quads
+#pragma unroll
+  for (int d = 0; d < kUnroll; ++d)
+    if (q0 + d < T.nq) quad(q0 + d, q0 + d + 1 < T.nq);
 
-  // epilogue: acc[mt][t][r] is row mt*16 + 4*lq + r of the pass, feature f[t]
+  // epilogue: acc[mt][t][r] is row mt*32 + 4h + (r%4) + 8(r/4) of the pass, feature f[t]
   const uint16_t *bias = g.bias + (int64_t)T.e * g.bias_stride;
   if (PHASE == 0) {
     if (T.tile_on[0]) {
       const float bg = bf16f(bias[T.f[0]]), bu = bf16f(bias[g.I + T.f[0]]);
 #pragma unroll
-      for (int mt = 0; mt < MTS; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mt * 16 + lq * 4 + r;
+        for (int r = 0; r < 16; ++r) {
+          const int m = mt * 32 + 4 * h + (r & 3) + 8 * (r >> 2);
           if (m < T.mrows) {
             const float gv = acc[mt][0][r] + bg, uv = acc[mt][1][r] + bu;
             const float hv = gv / (1.f + __expf(-gv)) * uv;
@@ -262,13 +295,13 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
       if (!T.tile_on[t]) continue;
       const float bd = bf16f(bias[T.f[t]]);
 #pragma unroll
-      for (int mt = 0; mt < MTS; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mt * 16 + lq * 4 + r;
+        for (int r = 0; r < 16; ++r) {
+          const int m = mt * 32 + 4 * h + (r & 3) + 8 * (r >> 2);
           if (m < T.mrows) {
-            const int p = g.perm[T.off + T.m0 + m];
-            g.obuf[(int64_t)p * g.H + T.f[t]] = acc[mt][t][r] + bd;
+            const int pr = g.perm[T.off + T.m0 + m];
+            g.obuf[(int64_t)pr * g.H + T.f[t]] = acc[mt][t][r] + bd;
           }
         }
       }
@@ -278,9 +311,10 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
 
 template <int PHASE>
 __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
-  constexpr int NFB = PHASE == 0 ? 64 : 128;  // features per block
+  constexpr int NFB = PHASE == 0 ? 128 : 256;  // features per block
   __shared__ __align__(16) uint16_t As[2][BM * LDA];
-  __shared__ int64_t rowoff[BM];
+  __shared__ int32_t rowoff[BM];
+  __shared__ __align__(16) uint8_t sc_lds[kMaxKb * kRowsB];
   Tile T;
   int nt;
   if (g.xcd) {
@@ -301,44 +335,59 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
   T.nkb = T.K / 32;
   T.nq = (T.nkb + 3) >> 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  T.l16 = lane & 15;
-  T.lq = lane >> 4;
-  const int fbase = nt * NFB + wave * (PHASE == 0 ? 16 : 32);
+  T.n32 = lane & 31;
+  T.h = lane >> 5;
   if (PHASE == 0) {
-    T.f[0] = T.f[1] = fbase + T.l16;
+    const int fbase = nt * NFB + wave * 32;
+    T.f[0] = T.f[1] = fbase + T.n32;
     T.nrow[0] = min(T.f[0], g.I - 1);
     T.nrow[1] = g.I + T.nrow[0];
+    T.lrow[0] = wave * 32 + T.n32;
+    T.lrow[1] = 128 + T.lrow[0];
     T.tile_on[0] = T.tile_on[1] = fbase < nfeat;
   } else {
-    T.f[0] = fbase + T.l16;
-    T.f[1] = T.f[0] + 16;
+    const int fbase = nt * NFB + wave * 64;
+    T.f[0] = fbase + T.n32;
+    T.f[1] = T.f[0] + 32;
     T.nrow[0] = min(T.f[0], T.N - 1);
     T.nrow[1] = min(T.f[1], T.N - 1);
+    T.lrow[0] = wave * 64 + T.n32;
+    T.lrow[1] = T.lrow[0] + 32;
     T.tile_on[0] = fbase < nfeat;
-    T.tile_on[1] = fbase + 16 < nfeat;
+    T.tile_on[1] = fbase + 32 < nfeat;
+  }
+  // scale bytes of the block's 256 weight rows: sc_lds[kb][local row], taken as
+  // dwords of four rows (rows past the matrix clamp to its last dword; their
+  // tiles are never stored)
+  {
+    const uint8_t *scl = g.scales + (int64_t)T.e * g.scales_stride;
+    for (int i = threadIdx.x; i < T.nkb * (kRowsB / 4); i += kThreads) {
+      const int kb = i / (kRowsB / 4), r4 = (i % (kRowsB / 4)) * 4;
+      int row;
+      if (PHASE == 0) row = r4 < 128 ? min(nt * 128 + r4, g.I - 4) : g.I + min(nt * 128 + r4 - 128, g.I - 4);
+      else row = min(nt * 256 + r4, T.N - 4);
+      *reinterpret_cast<uint32_t *>(&sc_lds[kb * kRowsB + r4]) =
+          *reinterpret_cast<const uint32_t *>(scl + (int64_t)kb * T.N + row);
+    }
   }
   const int lda_src = PHASE == 0 ? g.H : g.I;
 
   for (T.m0 = 0; T.m0 < m_e; T.m0 += BM) {
     T.mrows = min(BM, m_e - T.m0);
-    __syncthreads();  // the previous pass is done with rowoff and As
+    __syncthreads();  // the previous pass is done with rowoff and As; sc_lds is written
     for (int r = threadIdx.x; r < BM; r += kThreads) {
-      int64_t o = -1;
+      int32_t o = -1;
       if (r < T.mrows) {
-        const int64_t src_row =
-            PHASE == 0 ? (int64_t)(g.perm[T.off + T.m0 + r] / g.k) : (int64_t)(T.off + T.m0 + r);
+        const int32_t src_row = PHASE == 0 ? g.perm[T.off + T.m0 + r] / g.k : T.off + T.m0 + r;
         o = src_row * lda_src;
       }
       rowoff[r] = o;
     }
     __syncthreads();
-    switch ((T.mrows + 15) >> 4) {
-      case 1: gemm_pass<PHASE, 1>(g, T, As, rowoff); break;
-      case 2: gemm_pass<PHASE, 2>(g, T, As, rowoff); break;
-      case 3: gemm_pass<PHASE, 3>(g, T, As, rowoff); break;
-      case 4: gemm_pass<PHASE, 4>(g, T, As, rowoff); break;
-      case 5: gemm_pass<PHASE, 5>(g, T, As, rowoff); break;
-      default: gemm_pass<PHASE, 6>(g, T, As, rowoff); break;
+    switch ((T.mrows + 31) >> 5) {
+      case 1: gemm_pass<PHASE, 1>(g, T, As, rowoff, sc_lds); break;
+      case 2: gemm_pass<PHASE, 2>(g, T, As, rowoff, sc_lds); break;
+      default: gemm_pass<PHASE, 3>(g, T, As, rowoff, sc_lds); break;
     }
   }
 }
@@ -394,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, co
 }
 
 struct WsLayout {
-  int64_t offsets, perm, hbuf, obuf, total;
+  int64_t offsets, zeros, perm, hbuf, obuf, total;
 };
 
 WsLayout ws_layout(int H, int I, int n, int k, int E) {
@@ -402,7 +451,8 @@ WsLayout ws_layout(int H, int I, int n, int k, int E) {
   WsLayout L;
   const int64_t nk = (int64_t)n * k;
   L.offsets = 0;
-  L.perm = up(4ll * (E + 1));
+  L.zeros = up(4ll * (E + 1));
+  L.perm = L.zeros + 256;
   L.hbuf = L.perm + up(4 * nk);
   L.obuf = L.hbuf + up(2 * nk * I);
   L.total = L.obuf + up(4 * nk * H);
@@ -418,12 +468,16 @@ hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t s) 
 
 int64_t mfma_probe_flops(int blocks, int iters) { return (int64_t)blocks * (kThreads / 64) * iters * 8 * 16 * 16 * 32 * 2; }
 
-bool prefill_supported(int H, int I, int E) { return H % 64 == 0 && I % 64 == 0 && E <= OES_MAX_EXPERTS; }
+bool prefill_supported(int H, int I, int E) {
+  return H % 64 == 0 && I % 64 == 0 && H / 32 <= kMaxKb && I / 32 <= kMaxKb && E <= OES_MAX_EXPERTS;
+}
 
 int64_t prefill_workspace_bytes(int H, int I, int n, int k, int E) { return ws_layout(H, I, n, k, E).total; }
 
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   if (!prefill_supported(a.H, a.I, a.E)) return hipErrorInvalidValue;
+  // A element offsets of the GEMMs are 32-bit
+  if ((int64_t)a.n * a.k * std::max(a.H, a.I) >= (int64_t)1 << 31) return hipErrorInvalidValue;
   const WsLayout L = ws_layout(a.H, a.I, a.n, a.k, a.E);
   if (a.ws_bytes < L.total) return hipErrorInvalidValue;
   const int nk = a.n * a.k;
@@ -431,11 +485,13 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   int32_t *perm = reinterpret_cast<int32_t *>(a.ws + L.perm);
   uint16_t *hbuf = reinterpret_cast<uint16_t *>(a.ws + L.hbuf);
   float *obuf = reinterpret_cast<float *>(a.ws + L.obuf);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm);
+  uint32_t *zeros = reinterpret_cast<uint32_t *>(a.ws + L.zeros);
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm, zeros);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   GemmArgs g;
+  g.zero16 = reinterpret_cast<const u32x4 *>(zeros);
   g.H = a.H;
   g.I = a.I;
   g.E = a.E;
@@ -454,7 +510,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   g.blocks_stride = a.row_bytes[0];
   g.scales_stride = a.row_bytes[1];
   g.bias_stride = a.row_bytes[2] / 2;
-  g.ntiles = (a.I + 63) / 64;
+  g.ntiles = (a.I + 127) / 128;
   hipLaunchKernelGGL(moe_gemm_kernel<0>, dim3(a.E * g.ntiles), dim3(kThreads), 0, s, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -465,7 +521,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   g.blocks_stride = a.row_bytes[3];
   g.scales_stride = a.row_bytes[4];
   g.bias_stride = a.row_bytes[5] / 2;
-  g.ntiles = (a.H + 127) / 128;
+  g.ntiles = (a.H + 255) / 256;
   hipLaunchKernelGGL(moe_gemm_kernel<1>, dim3(a.E * g.ntiles), dim3(kThreads), 0, s, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
