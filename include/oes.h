@@ -308,7 +308,7 @@ oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x, const int
  *   host memory into device memory (the zero-copy path's ceiling).
  * oes_probe_hbm_read: a streaming read of `bytes` of device memory.
  * oes_probe_mfma_bf16: `blocks` workgroups of 4 waves, each wave `iters` rounds of
- *   8 independent v_mfma_f32_16x16x32_bf16 (the prefill GEMM's instruction) on
+ *   4 independent v_mfma_f32_32x32x16_bf16 (the prefill GEMM's instruction) on
  *   register operands; `*flops` receives the dense flops issued.  `sink` is a
  *   device float the kernel may write (it never does in practice).  blocks >= 1,
  *   1 <= iters <= 1 << 24. */

@@ -385,7 +385,7 @@ def probe_hbm_read(dev, nbytes, sink, stream=None):
 
 
 def probe_mfma_bf16(blocks, iters, sink, stream=None):
-    """(ms, flops) of the bf16 MFMA loop: blocks x 4 waves x iters x 8 MFMAs."""
+    """(ms, flops) of the bf16 MFMA loop: blocks x 4 waves x iters x 4 chained 32x32x16 MFMAs."""
     ms, flops = ctypes.c_float(), ctypes.c_double()
     _check(lib().oes_probe_mfma_bf16(blocks, iters, _ptr(sink), _stream(stream), ctypes.byref(ms), ctypes.byref(flops)))
     return ms.value, flops.value

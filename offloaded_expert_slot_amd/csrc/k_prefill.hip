@@ -53,6 +53,7 @@ constexpr int kThreads = 256;
 constexpr int BM = 96;             // rows per pass: three 32-row m-tiles
 constexpr int LDA = 128 + 8;       // LDS row of one 128-k quad, bf16 elements, padded 16 B
 constexpr int kXcds = 8;
+constexpr int kProbeChains = 4;    // accumulator chains per wave of the MFMA ceiling probe
 constexpr int kMaxKb = 96;         // K / 32 limit of the grouped GEMM (K <= 3072)
 static_assert(kThreads == 256, "two A pieces per thread cover one row of each half m-tile");
 
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ MFMA ceiling
-// Eight independent accumulator chains of v_mfma_f32_16x16x32_bf16 per wave, the
+// Four independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave, the
 // instruction the grouped GEMM uses; operands stay in registers.  The result is
 // stored only on an impossible value, which keeps the chains live.
 __global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *sink) {
@@ -404,16 +405,18 @@ __global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *
     a[i] = (__bf16)(0.001f * (float)(lane + i));
     b[i] = (__bf16)(0.002f * (float)(lane - i));
   }
-  f32x4 acc[8];
+  f32x16 acc[kProbeChains];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4{(float)c, 0.f, 0.f, 0.f};
+  for (int c = 0; c < kProbeChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = (float)(c + r);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+    for (int c = 0; c < kProbeChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
   }
   float t = 0.f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) t += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  for (int c = 0; c < kProbeChains; ++c) t += acc[c][0] + acc[c][15];
   if (t == 1234.5678f) sink[0] = t;
 }
 
@@ -466,7 +469,9 @@ hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t s) 
   return hipGetLastError();
 }
 
-int64_t mfma_probe_flops(int blocks, int iters) { return (int64_t)blocks * (kThreads / 64) * iters * 8 * 16 * 16 * 32 * 2; }
+int64_t mfma_probe_flops(int blocks, int iters) {
+  return (int64_t)blocks * (kThreads / 64) * iters * kProbeChains * 32 * 32 * 16 * 2;
+}
 
 bool prefill_supported(int H, int I, int E) {
   return H % 64 == 0 && I % 64 == 0 && H / 32 <= kMaxKb && I / 32 <= kMaxKb && E <= OES_MAX_EXPERTS;
