@@ -12,7 +12,8 @@ One "step" = route -> ensure_experts -> copy_missing -> expert_ffn for one
 token (bs=1), with the slot table restored on the device (untimed) before each
 step so that misses = round(active * miss_rate) of the routed experts miss.
 Steps are enqueued back to back and each is timed with HIP events on the
-launch stream; value = 1000 / (L * ms_per_step).
+launch stream at its two ends; value = 1000 / (L * ms_per_step).  A second pass
+with events between the four parts gives the breakdown and the copy's time.
 
 Also printed (same JSON line): the copy sweep of the benchmark guide's columns
 (bs, active, miss_rate, misses, time_ms, copy_MiB, bw_GBps, tok_ms; median of
@@ -99,11 +100,18 @@ def main():
         sink = torch.zeros(4, dtype=torch.float32, device=dev)
         hbm = [oes.probe_hbm_read(big, big.numel(), sink) for _ in range(5)]
         mfma = [oes.probe_mfma_bf16(2048, 10000, sink) for _ in range(3)]
+        # streaming reads of the FFN's byte count, back to back over 16 distinct
+        # regions (1.2 GB), timed like the FFN alone below
+        fb = (w.k * bpe // 16) * 16
+        fstride = (fb + 4095) // 4096 * 4096
+        hbm_small = [oes.probe_hbm_read(big, fb, sink, stride=fstride, count=16) for _ in range(4)]
         probes = {
             "h2d_dma_GBps": nbytes / (min(dma) * 1e6),
             "h2d_zero_copy_GBps": nbytes / (min(zc) * 1e6),
             "hbm_read_GBps": big.numel() / (min(hbm) * 1e6),
             "mfma_bf16_TFLOPs": max(fl / (ms * 1e9) for ms, fl in mfma),
+            "hbm_read_ffn_bytes_GBps": fb / (min(hbm_small) * 1e6),
+            "ffn_bytes": fb,
             "h2d_bytes": nbytes,
         }
         probes["h2d_peak_GBps"] = max(probes["h2d_dma_GBps"], probes["h2d_zero_copy_GBps"])
@@ -131,48 +139,59 @@ def main():
         owner, stamp, clock, pre = synth.forced_miss_state(w.S, w.E, 0, routed, misses)
         return misses, owner, stamp, clock, pre
 
-    def run_steps(mr, steps, warmup):
+    def run_steps(mr, steps, warmup, parts):
+        """Enqueue warmup + steps layer steps back to back, the slot table restored
+        on the device between steps (outside the events).  parts=False: events
+        only at step boundaries (each event recorded inside a step idles the GPU
+        for several microseconds); parts=True: also between route, ensure, copy
+        and FFN, for the breakdown."""
         misses, owner, stamp, clock, pre = prepare(mr)
         cache.set_state(owner, stamp, clock)
         if pre:
             cache.load_rows([p[0] for p in pre], [p[1] for p in pre])
         cache.snapshot()
         torch.cuda.synchronize()
-        # steps are enqueued back to back; the table is restored on the device
-        # between steps (outside the timed events), so the host never stalls the GPU
         rec = []
         for i in range(warmup + steps):
             cache.restore()
-            e = [ev() for _ in range(5)]
+            e = [ev() for _ in range(5 if parts else 2)]
             e[0].record(stream)
             oes.route(x, wg, w.k, ids, wts, rws)
-            e[1].record(stream)
+            if parts:
+                e[1].record(stream)
             cache.ensure_experts(0, ids, slot_ids)
-            e[2].record(stream)
+            if parts:
+                e[2].record(stream)
             cache.copy_missing()
-            e[3].record(stream)
+            if parts:
+                e[3].record(stream)
             cache.expert_ffn(x, slot_ids, wts, y, fws)
-            e[4].record(stream)
+            e[-1].record(stream)
             if i >= warmup:
                 rec.append(e)
         torch.cuda.synchronize()
         cache.check()
-        parts = np.array([[r[j].elapsed_time(r[j + 1]) for j in range(4)] for r in rec])
-        total = np.array([r[0].elapsed_time(r[4]) for r in rec])
-        return misses, total, parts
+        total = np.array([r[0].elapsed_time(r[-1]) for r in rec])
+        if not parts:
+            return misses, total, None
+        return misses, total, np.array([[r[j].elapsed_time(r[j + 1]) for j in range(4)] for r in rec])
 
     per_mr = []
     headline = None
     # the headline miss rate runs first, so that its copy launches are the first
-    # gather dispatches of the run (the profile summary averages exactly those)
+    # gather dispatches of the run: 0..W+K-1 the timed pass, W+K..2(W+K)-1 the
+    # breakdown pass (the profile summary averages the latter's timed ones)
     rates = [args.miss_rate] + [r for r in sorted(w.miss_rates) if abs(r - args.miss_rate) > 1e-12]
     for mr in rates:
         is_head = abs(mr - args.miss_rate) < 1e-12
         steps = args.steps if is_head else max(5, args.steps // 3)
-        misses, total, parts = run_steps(mr, steps, args.warmup if is_head else 2)
+        wu = args.warmup if is_head else 2
+        misses, total, _ = run_steps(mr, steps, wu, parts=False)
+        _, ptotal, parts = run_steps(mr, steps, wu, parts=True)
         ms = float(total.mean())
         row = {"miss_rate": mr, "misses": misses, "ms_per_step": ms, "ms_median": float(np.median(total)),
                "tok_ms": ms * w.L, "decode_tok_s": 1000.0 / (w.L * ms),
+               "ms_per_step_with_part_events": float(ptotal.mean()),
                "route_ms": float(parts[:, 0].mean()), "ensure_ms": float(parts[:, 1].mean()),
                "copy_ms": float(parts[:, 2].mean()), "ffn_ms": float(parts[:, 3].mean())}
         if misses:
@@ -182,6 +201,30 @@ def main():
         if is_head:
             headline = (row, total, parts)
         log("decode", {k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()})
+
+    # FFN alone (HBM roofline): back-to-back launches, each on one of 16 slot maps
+    # of 8 distinct slots (128 slots, 1.2 GB in all), so that no launch finds its
+    # rows in the 256 MB memory-side cache from the previous ones, as in a real
+    # token where every layer has other experts.  Slot contents do not matter for
+    # the time; the step loop above keeps its own state.
+    rng = np.random.default_rng(0)
+    nsets = 16
+    pool = rng.permutation(w.S)[: nsets * w.k]
+    maps = [torch.from_numpy(pool[i * w.k:(i + 1) * w.k].astype(np.int32).reshape(1, w.k)).to(dev)
+            for i in range(nsets)]
+    for i in range(4):
+        cache.expert_ffn(x, maps[i], wts, y, fws)
+    a, b = ev(), ev()
+    n_ffn = 64
+    a.record(stream)
+    for i in range(n_ffn):
+        cache.expert_ffn(x, maps[i % nsets], wts, y, fws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    cache.check()
+    ffn_alone_ms = a.elapsed_time(b) / n_ffn
+    ffn_bytes = w.k * bpe
+    log("ffn", {"launches": n_ffn, "slot_maps": nsets, "ms_per_launch": round(ffn_alone_ms, 5)})
 
     # ---------------------------------------------------------------- copy sweep
     sweep = []
@@ -224,13 +267,15 @@ def main():
 
     # ---------------------------------------------------------------- rooflines
     head, total, parts = headline
-    ffn_row = next(r for r in per_mr if r["misses"] == 0) if any(r["misses"] == 0 for r in per_mr) else head
-    ffn_gbs = u_bytes / (ffn_row["ffn_ms"] * 1e6)
+    ffn_gbs = ffn_bytes / (ffn_alone_ms * 1e6)
     kernels = {
         "expert_ffn": {"bound": "hbm", "achieved": ffn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": ffn_gbs / HBM_PEAK_GBS, "bytes_per_launch": u_bytes,
-                       "avg_ms": ffn_row["ffn_ms"], "traffic": _pmc_traffic("expert_ffn")},
+                       "frac": ffn_gbs / HBM_PEAK_GBS, "bytes_per_launch": ffn_bytes,
+                       "avg_ms": ffn_alone_ms, "traffic": _pmc_traffic("expert_ffn")},
     }
+    if probes:
+        kernels["expert_ffn"]["frac_of_measured_hbm_read"] = ffn_gbs / probes["hbm_read_GBps"]
+        kernels["expert_ffn"]["frac_of_hbm_read_same_bytes"] = ffn_gbs / probes["hbm_read_ffn_bytes_GBps"]
     if head["misses"]:
         cbytes = head["misses"] * bpe
         cgbs = cbytes / (head["copy_ms"] * 1e6)

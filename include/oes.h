@@ -306,7 +306,11 @@ oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x, const int
  * oes_probe_h2d_dma: one hipMemcpyAsync of `bytes` from pinned host to device.
  * oes_probe_h2d_kernel: the gather kernel's read of `bytes` of mapped pinned
  *   host memory into device memory (the zero-copy path's ceiling).
- * oes_probe_hbm_read: a streaming read of `bytes` of device memory.
+ * oes_probe_hbm_read: `count` streaming reads of `bytes` each, launched back to
+ *   back, the i-th at dev + i * stride (a stride that walks past the 256 MB
+ *   memory-side cache keeps every read cold); *ms is the time per read.  The
+ *   caller's buffer spans (count - 1) * stride + bytes; bytes and stride are
+ *   multiples of 16, count >= 1.
  * oes_probe_mfma_bf16: `blocks` workgroups of 4 waves, each wave `iters` rounds of
  *   4 independent v_mfma_f32_32x32x16_bf16 (the prefill GEMM's instruction) on
  *   register operands; `*flops` receives the dense flops issued.  `sink` is a
@@ -315,7 +319,8 @@ oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x, const int
 oes_status oes_probe_h2d_dma(void *dev, const void *host, int64_t bytes, void *stream, float *ms);
 oes_status oes_probe_h2d_kernel(void *dev, const void *host, int64_t bytes, int32_t blocks,
                                 void *stream, float *ms);
-oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, void *sink, void *stream, float *ms);
+oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, int64_t stride, int32_t count, void *sink,
+                              void *stream, float *ms);
 oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
                                double *flops);
 

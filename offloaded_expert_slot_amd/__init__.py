@@ -108,7 +108,7 @@ _SIGS = {
     "oes_layers_ffn": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I64, _P]),
     "oes_probe_h2d_dma": (_I32, [_P, _P, _I64, _P, _PF]),
     "oes_probe_h2d_kernel": (_I32, [_P, _P, _I64, _I32, _P, _PF]),
-    "oes_probe_hbm_read": (_I32, [_P, _I64, _P, _P, _PF]),
+    "oes_probe_hbm_read": (_I32, [_P, _I64, _I64, _I32, _P, _P, _PF]),
     "oes_probe_mfma_bf16": (_I32, [_I32, _I32, _P, _P, _PF, ctypes.POINTER(ctypes.c_double)]),
     "oes_debug_decode": (_I32, [_I32, _P, _I32, _P, _P]),
 }
@@ -378,9 +378,10 @@ def probe_h2d_kernel(dev, host, nbytes, blocks=1024, stream=None):
     return ms.value
 
 
-def probe_hbm_read(dev, nbytes, sink, stream=None):
+def probe_hbm_read(dev, nbytes, sink, stride=0, count=1, stream=None):
+    """ms per read of `count` back-to-back streaming reads of nbytes, the i-th at dev + i*stride."""
     ms = ctypes.c_float()
-    _check(lib().oes_probe_hbm_read(_ptr(dev), nbytes, _ptr(sink), _stream(stream), ctypes.byref(ms)))
+    _check(lib().oes_probe_hbm_read(_ptr(dev), nbytes, stride, count, _ptr(sink), _stream(stream), ctypes.byref(ms)))
     return ms.value
 
 

@@ -992,16 +992,21 @@ extern "C" oes_status oes_probe_h2d_kernel(void *dev, const void *host, int64_t 
   return timed(s, ms, e0, e1);
 }
 
-extern "C" oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, void *sink, void *stream, float *ms) {
-  if (!dev || bytes <= 0 || bytes % 16 || !sink || !ms) return fail(OES_ERR_ARG, "bad probe arguments");
+extern "C" oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, int64_t stride, int32_t count, void *sink,
+                                         void *stream, float *ms) {
+  if (!dev || bytes <= 0 || bytes % 16 || stride < 0 || stride % 16 || count < 1 || !sink || !ms)
+    return fail(OES_ERR_ARG, "bad probe arguments");
   hipStream_t s = as_stream(stream);
   hipEvent_t e0, e1;
   HIP_TRY(hipEventCreate(&e0));
   HIP_TRY(hipEventCreate(&e1));
   HIP_TRY(hipEventRecord(e0, s));
-  HIP_TRY(launch_hbm_read(static_cast<const uint8_t *>(dev), bytes, static_cast<float *>(sink), s));
+  for (int32_t i = 0; i < count; ++i)
+    HIP_TRY(launch_hbm_read(static_cast<const uint8_t *>(dev) + (int64_t)i * stride, bytes, static_cast<float *>(sink), s));
   HIP_TRY(hipEventRecord(e1, s));
-  return timed(s, ms, e0, e1);
+  const oes_status st = timed(s, ms, e0, e1);
+  if (st == OES_OK) *ms /= (float)count;
+  return st;
 }
 
 extern "C" oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,

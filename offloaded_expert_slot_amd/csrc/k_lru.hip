@@ -35,6 +35,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPerThread = OES_MAX_EXPERTS / kThreads;  // 4 experts per thread in the scan
 constexpr uint64_t kMax = ~0ull;
+constexpr int kSelectMax = 2;  // misses up to which victims are selected rather than sorted (measured crossover)
 
 // Block-wide exclusive scan of one int per thread; returns the exclusive prefix, *total the sum.
 __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
@@ -166,6 +167,73 @@ __device__ void sort_victims(const LruArgs &a, const uint8_t *req, int64_t base,
   __syncthreads();
 }
 
+// The m smallest victim keys, ascending, into khi / klo[0..m): m rounds of a
+// block-wide minimum (wave shuffles, then the 16 wave minima from LDS); the
+// thread holding the minimum drops it.  Keys are unique (the slot is in the low
+// bits), so this equals the first m entries of the full sort; for a few misses
+// it avoids sorting the whole pool.  m <= slots not holding a member of U
+// (guaranteed by the capacity check), so every selected key is a real slot.
+template <int R>
+__device__ void select_victims(const LruArgs &a, const uint8_t *req, int64_t base, int m, uint64_t *khi,
+                               uint64_t *klo, uint64_t *wmin_h, uint64_t *wmin_l) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t hi[R], lo[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int s = threadIdx.x + r * kThreads;
+    hi[r] = kMax;
+    lo[r] = kMax;
+    if (s < a.S) {
+      const int64_t o = a.owner[s];
+      const bool in_u = o >= base && o < base + a.E && req[(int)(o - base)];
+      if (!in_u) {
+        hi[r] = ((o != -1) ? (1ull << 63) : 0ull) | a.stamp[s];
+        lo[r] = ((uint64_t)(o + 1) << 12) | (uint64_t)s;
+      }
+    }
+  }
+  for (int i = 0; i < m; ++i) {
+    uint64_t bh = hi[0], bl = lo[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r)
+      if (key_less(hi[r], lo[r], bh, bl)) {
+        bh = hi[r];
+        bl = lo[r];
+      }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const uint64_t ph = shfl_xor_u64(bh, d), pl = shfl_xor_u64(bl, d);
+      if (key_less(ph, pl, bh, bl)) {
+        bh = ph;
+        bl = pl;
+      }
+    }
+    if (lane == 0) {
+      wmin_h[wave] = bh;
+      wmin_l[wave] = bl;
+    }
+    __syncthreads();
+    uint64_t gh = wmin_h[0], gl = wmin_l[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+      if (key_less(wmin_h[w], wmin_l[w], gh, gl)) {
+        gh = wmin_h[w];
+        gl = wmin_l[w];
+      }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (hi[r] == gh && lo[r] == gl) {
+        hi[r] = kMax;
+        lo[r] = kMax;
+      }
+    if (threadIdx.x == 0) {
+      khi[i] = gh;
+      klo[i] = gl;
+    }
+    __syncthreads();  // the wave minima are rewritten next round
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   __shared__ uint64_t khi[OES_MAX_SLOTS];
   __shared__ uint64_t klo[OES_MAX_SLOTS];
@@ -173,6 +241,7 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   __shared__ int32_t mrank[OES_MAX_EXPERTS];
   __shared__ uint8_t req[OES_MAX_EXPERTS];
   __shared__ int wave_tot[kWaves + 1];
+  __shared__ uint64_t wmin_h[kWaves], wmin_l[kWaves];
   __shared__ int s_bad, s_evict;
   __shared__ uint64_t s_clock;
 
@@ -244,13 +313,22 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   }
 
   if (nM > 0) {
-    // 4-5. victim keys sorted ascending (slots holding a member of U sort last)
-    if (a.Spad <= kThreads)
+    // 4-5. victim keys ascending (slots holding a member of U sort last): the
+    // first nM of them, by selection for a few misses, else by a full sort
+    if (nM <= kSelectMax) {
+      if (a.Spad <= kThreads)
+        select_victims<1>(a, req, base, nM, khi, klo, wmin_h, wmin_l);
+      else if (a.Spad <= 2 * kThreads)
+        select_victims<2>(a, req, base, nM, khi, klo, wmin_h, wmin_l);
+      else
+        select_victims<4>(a, req, base, nM, khi, klo, wmin_h, wmin_l);
+    } else if (a.Spad <= kThreads) {
       sort_victims<1>(a, req, base, khi, klo);
-    else if (a.Spad <= 2 * kThreads)
+    } else if (a.Spad <= 2 * kThreads) {
       sort_victims<2>(a, req, base, khi, klo);
-    else
+    } else {
       sort_victims<4>(a, req, base, khi, klo);
+    }
     // 6. install: the i-th miss takes the i-th victim
     for (int e = tid; e < E; e += kThreads) {
       const int r = mrank[e];

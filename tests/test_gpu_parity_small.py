@@ -114,6 +114,22 @@ def test_lru_large_pool_and_seeded_state():
     _lru_trace(S, L, E, steps, (owner, stamp, 5))
 
 
+def test_lru_pool_over_2048_slots():
+    """Four keys per thread: victims selected (few misses) and sorted (many)."""
+    rng = np.random.default_rng(23)
+    L, E, S = 6, 700, 3000
+    owner = np.full(S, -1, dtype=np.int64)
+    ids = rng.choice(L * E, size=2600, replace=False)
+    owner[rng.choice(S, size=2600, replace=False)] = ids
+    stamp = rng.integers(0, 7, size=S).astype(np.uint64)
+    _case("lru S=3000 E=700 seeded state")
+    steps = []
+    for i in range(24):
+        rows = 1 if i % 3 else 12          # 8 or 96 routed ids per step
+        steps.append((int(rng.integers(L)), rng.integers(0, E, size=(rows, 8)).tolist()))
+    _lru_trace(S, L, E, steps, (owner, stamp, 7))
+
+
 def test_lru_capacity_and_bad_ids_leave_state():
     _case("lru capacity / bad id")
     steps = [(0, [[0, 1]]), (0, [[0, 1, 2, 3]]), (0, [[5]]), (0, [[-1]]), (0, [[2, 3]])]
