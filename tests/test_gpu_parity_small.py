@@ -250,6 +250,12 @@ FFN_CASES = [
     ("bf16", 2048, 768, 8, 8, 1), ("fp8_block128", 256, 256, 8, 2, 3), ("fp8_block128", 512, 256, 9, 4, 2),
     ("nvfp4", 256, 256, 8, 2, 3), ("nvfp4", 512, 256, 7, 4, 2), ("nvfp4", 7168, 256, 4, 2, 1),
 ]
+# the decode workloads' subgroup shapes (32-lane gate_up and down subgroups),
+# with 1, 3, 1, 1, 2 and 4 chunks of a down row per lane, at several tokens
+FFN_CASES += [
+    ("bf16", 1536, 256, 12, 8, 5), ("bf16", 2048, 768, 8, 8, 5), ("fp8_block128", 4096, 512, 8, 6, 3),
+    ("nvfp4", 7168, 1024, 8, 5, 2), ("bf16", 2048, 512, 8, 8, 3), ("bf16", 2048, 1024, 9, 8, 4),
+]
 
 
 @pytest.mark.parametrize("fmt,H,I,E,k,n", FFN_CASES)
@@ -274,7 +280,9 @@ def test_expert_ffn_matches_oracle(fmt, H, I, E, k, n):
     d_w = torch.from_numpy(w).to(G.dev())
     y = torch.empty((n, H), dtype=torch.int16, device=G.dev())
     ws = torch.empty(c.ffn_workspace_bytes(n, k), dtype=torch.uint8, device=G.dev())
+    y2 = torch.empty_like(y)
     c.expert_ffn(x, d_slots, d_w, y, ws)
+    c.expert_ffn(x, d_slots, d_w, y2, ws)
     torch.cuda.synchronize()
     c.check()
     ref = offn.expert_ffn(fmt, H, I, G.bits16(x), slot_ids, w.astype(np.float64),
@@ -286,6 +294,8 @@ def test_expert_ffn_matches_oracle(fmt, H, I, E, k, n):
     assert err <= tol
     # a tighter bound than the contract: bf16 output rounding plus bf16 intermediate
     assert err <= 5e-3
+    # the FFN is deterministic: both launches give the same bits
+    assert torch.equal(y, y2)
 
 
 def test_ffn_gated_off_after_failed_step():
