@@ -49,3 +49,13 @@ def decode_tok_s(step_ms: float, num_layers: int) -> float:
     if step_ms <= 0.0:
         raise ValueError("step_ms must be positive")
     return 1000.0 / (num_layers * step_ms)
+
+
+def hybrid_fetch_fraction(pcie_gbps: float, cpu_gbps: float) -> float:
+    """Share of a step's misses a hybrid step fetches over PCIe (FreeToken MoE
+    benchmark guide §5.4): overlap is ideal when fetched : CPU-computed experts
+    = pcie_bw : (cpu_bw - pcie_bw), i.e. a fetched share of pcie_bw / cpu_bw;
+    with a CPU no faster than the link every miss is fetched."""
+    if cpu_gbps <= pcie_gbps:
+        return 1.0
+    return pcie_gbps / cpu_gbps

@@ -34,10 +34,25 @@ OK, ERR_ARG, ERR_CAPACITY = 0, -1, -2
 @dataclass
 class EnsureResult:
     status: int
-    slot_ids: np.ndarray = None          # int32 [n, k], slot owning each request
+    slot_ids: np.ndarray = None          # int32 [n, k], slot owning each request (-1: not fetched)
     misses: list = field(default_factory=list)   # [(slot, flat_id)] in install order
     hits: int = 0
     evictions: int = 0                   # misses that displaced a non-empty slot
+    num_indices: int = 0                 # hybrid: misses fetched this step (within the cap)
+    num_missing_full: int = 0            # hybrid: misses before the cap
+    overflow: list = field(default_factory=list)  # hybrid: flat ids left to the CPU executor, ascending
+
+
+def hybrid_cap(num_missing_full: int, max_fetch: int, fetch_fraction=None) -> int:
+    """Fetch cap of a hybrid step (FreeToken MoE benchmark guide §5.4): an explicit
+    hybrid_max_fetch >= 0 is the cap; otherwise the measured fetch fraction
+    (pcie_bw / cpu_bw, at most 1) of this step's misses, rounded half to even;
+    with no fraction (no bandwidth profile) a fixed cap of one."""
+    if max_fetch >= 0:
+        return int(max_fetch)
+    if fetch_fraction is None or fetch_fraction < 0:
+        return 1
+    return int(round(num_missing_full * min(1.0, float(fetch_fraction))))
 
 
 class SlotTable:
@@ -97,3 +112,42 @@ class SlotTable:
         slot_ids = np.vectorize(lambda f: where[int(f)], otypes=[np.int64])(flat).astype(np.int32)
         return EnsureResult(status=OK, slot_ids=slot_ids, misses=installs,
                             hits=len(U) - len(missing), evictions=evictions)
+
+    def ensure_hybrid(self, layer: int, ids, max_fetch: int = -1, fetch_fraction=None) -> EnsureResult:
+        """ensure_experts_hybrid (FreeToken MoE benchmark guide §5.4): only the first
+        cap missing ids (ascending) get slots and copies; the others keep no slot,
+        their requests map to -1 and they go to the CPU executor.  Readings: the
+        cap is hybrid_cap(); it is further bounded by the evictable slots, so a
+        hybrid step never fails for capacity; ids left to the CPU are not stamped
+        (they own no slot); the clock advances as in ensure()."""
+        ids = np.asarray(ids, dtype=np.int64)
+        if ids.ndim == 1:
+            ids = ids[None, :]
+        if not (0 <= layer < self.L) or ids.size and (ids.min() < 0 or ids.max() >= self.E):
+            return EnsureResult(status=ERR_ARG)
+        flat = layer * self.E + ids
+        U = sorted(set(int(f) for f in flat.ravel()))
+        in_U = set(U)
+        where = {int(o): s for s, o in enumerate(self.owner) if o >= 0}
+        missing = [u for u in U if u not in where]
+        evictable = [s for s in range(self.S) if int(self.owner[s]) not in in_U]
+        evictable.sort(key=lambda s: (int(self.owner[s]) != -1, int(self.stamp[s]),
+                                      int(self.owner[s]), s))
+        take = min(hybrid_cap(len(missing), max_fetch, fetch_fraction), len(missing), len(evictable))
+        fetched, overflow = missing[:take], missing[take:]
+        installs, evictions = [], 0
+        for i, u in enumerate(fetched):
+            s = evictable[i]
+            if self.owner[s] != -1:
+                evictions += 1
+            self.owner[s] = u
+            where[u] = s
+            installs.append((s, u))
+        self.clock += 1
+        for u in U:
+            if u in where:
+                self.stamp[where[u]] = np.uint64(self.clock)
+        slot_ids = np.vectorize(lambda f: where.get(int(f), -1), otypes=[np.int64])(flat).astype(np.int32)
+        return EnsureResult(status=OK, slot_ids=slot_ids, misses=installs, hits=len(U) - len(missing),
+                            evictions=evictions, num_indices=take, num_missing_full=len(missing),
+                            overflow=overflow)

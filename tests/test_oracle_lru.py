@@ -7,6 +7,10 @@
 3. Invariants: every requested id resident afterwards, owners unique, no
    member of the request evicted, copies == misses, capacity failure leaves the
    state unchanged, only cold misses when the pool holds every id.
+4. ensure_experts_hybrid: a hand-worked trace (tests/golden/
+   lru_hybrid_trace_s3_e4.txt); on random traces it equals the plain LRU step on
+   the requests that keep a slot (overflow pairs map to -1); with a cap at or
+   above the misses it equals the plain step; the cap's closed forms.
 """
 import itertools
 import os
@@ -17,7 +21,7 @@ import pytest
 
 from oracle import copy as ocopy
 from oracle import formulas
-from oracle.lru import ERR_ARG, ERR_CAPACITY, OK, SlotTable
+from oracle.lru import ERR_ARG, ERR_CAPACITY, OK, SlotTable, hybrid_cap
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -214,3 +218,82 @@ def test_zero_and_full_miss_rate():
     active = formulas.active_unique(n, k, E)
     assert formulas.num_misses(active, 0.0) == 0
     assert formulas.num_misses(active, 1.0) == active
+
+
+# ------------------------------------------------------------------ hybrid
+def test_hybrid_hand_worked_trace():
+    lines = [l.split("#")[0].strip() for l in open(os.path.join(GOLDEN, "lru_hybrid_trace_s3_e4.txt"))]
+    lines = [l for l in lines if l]
+    pool = dict(kv.split("=") for kv in lines[0].split()[1:])
+    t = SlotTable(int(pool["S"]), int(pool["L"]), int(pool["E"]))
+    init = dict(kv.split("=") for kv in lines[1].split()[1:])
+    t.set_state(_ints(init["owner"]), _ints(init["stamp"]), int(init["clock"]))
+    for line in lines[2:]:
+        lhs, rhs = line.split("->")
+        _, layer, ids, mf, frac = lhs.split()
+        slots, misses, over, ni, nf, owner, stamp, clock, ev = [p.strip() for p in rhs.split("|")]
+        r = t.ensure_hybrid(int(layer), _rows(ids), int(mf), None if frac == "-" else float(frac))
+        assert r.status == OK, line
+        assert r.slot_ids.tolist() == _rows(slots), line
+        want = [] if misses == "-" else [tuple(int(v) for v in m.split(":")) for m in misses.split()]
+        assert r.misses == want, line
+        assert r.overflow == (_ints(over) or []), line
+        assert (r.num_indices, r.num_missing_full, r.evictions) == (int(ni), int(nf), int(ev)), line
+        assert t.owner.tolist() == _ints(owner), line
+        assert t.stamp.tolist() == _ints(stamp), line
+        assert t.clock == int(clock), line
+
+
+def test_hybrid_cap_closed_forms():
+    assert hybrid_cap(7, 3) == 3 and hybrid_cap(7, 0) == 0 and hybrid_cap(2, 9) == 9
+    assert hybrid_cap(7, -1) == 1 and hybrid_cap(0, -1) == 1          # no profile: a fixed cap of one
+    assert hybrid_cap(5, -1, 0.5) == 2 and hybrid_cap(3, -1, 0.5) == 2  # 2.5 -> 2, 1.5 -> 2 (half to even)
+    assert hybrid_cap(4, -1, 2.0) == 4 and hybrid_cap(8, -1, 0.0) == 0
+    assert formulas.hybrid_fetch_fraction(25.0, 100.0) == 0.25
+    assert formulas.hybrid_fetch_fraction(55.0, 50.0) == 1.0
+    # the ideal overlap of the pages: fetched : cpu = pcie : (cpu - pcie)
+    f = formulas.hybrid_fetch_fraction(30.0, 80.0)
+    assert abs(f / (1 - f) - 30.0 / (80.0 - 30.0)) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_hybrid_equals_plain_step_on_kept_requests(seed):
+    rng = random.Random(seed)
+    S, L, E = rng.randint(2, 12), rng.randint(1, 3), rng.randint(3, 16)
+    th, tp = SlotTable(S, L, E), SlotTable(S, L, E)
+    for _ in range(60):
+        layer = rng.randrange(L)
+        k = rng.randint(1, 4)
+        ids = np.array([[rng.randrange(E) for _ in range(k)] for _ in range(rng.randint(1, 3))])
+        mf = rng.choice([-1, 0, 1, 2, 5])
+        frac = rng.choice([None, 0.0, 0.25, 0.5, 1.0])
+        r = th.ensure_hybrid(layer, ids, mf, frac)
+        assert r.status == OK
+        over = set(r.overflow)
+        assert len(over) == r.num_missing_full - r.num_indices
+        keep = [[int(v) for v in row if layer * E + int(v) not in over] for row in ids]
+        flat_keep = [v for row in keep for v in row]
+        if flat_keep:
+            rp = tp.ensure(layer, np.array([flat_keep]))
+            assert rp.status == OK
+            assert rp.misses == r.misses
+            got = [s for row in r.slot_ids.tolist() for s in row if s >= 0]
+            assert got == rp.slot_ids.ravel().tolist()
+        else:
+            tp.clock += 1            # a step that keeps nothing still advances the clock
+        assert all(s == -1 for row, srow in zip(ids, r.slot_ids.tolist()) for v, s in zip(row, srow)
+                   if layer * E + int(v) in over)
+        assert np.array_equal(th.owner, tp.owner) and np.array_equal(th.stamp, tp.stamp) and th.clock == tp.clock
+
+
+def test_hybrid_without_cap_equals_plain():
+    rng = random.Random(9)
+    S, L, E = 10, 2, 8
+    th, tp = SlotTable(S, L, E), SlotTable(S, L, E)
+    for _ in range(40):
+        layer = rng.randrange(L)
+        ids = np.array([[rng.randrange(E) for _ in range(3)] for _ in range(2)])
+        r, rp = th.ensure_hybrid(layer, ids, 64), tp.ensure(layer, ids)
+        assert rp.status == OK and r.status == OK and r.overflow == []
+        assert r.slot_ids.tolist() == rp.slot_ids.tolist() and r.misses == rp.misses
+        assert r.num_indices == r.num_missing_full == len(rp.misses)
