@@ -116,8 +116,11 @@ typedef struct {
   uint64_t misses;        /* distinct requested ids installed */
   uint64_t evictions;     /* misses that displaced a non-empty slot */
   uint64_t bytes_copied;  /* misses * bytes_per_expert */
-  uint32_t last_misses;   /* misses of the last successful step */
+  uint32_t last_misses;   /* misses of the last successful step (installed ones) */
   int32_t failed_steps;   /* ensure_experts calls that failed on the device */
+  uint32_t last_indices;       /* misses fetched by the last step (num_indices) */
+  uint32_t last_missing_full;  /* misses of the last step before a hybrid cap (num_missing_full) */
+  uint64_t cpu_experts;        /* hybrid: misses left to the CPU executor, summed */
 } oes_stats;
 
 /* Create a slot cache of num_slots experts on HIP device `device`
@@ -244,6 +247,22 @@ oes_status oes_route_logits(const float *logits, int32_t n, int32_t num_experts,
  * Async. */
 oes_status oes_ensure_experts(oes_cache *c, int32_t layer, const int32_t *ids, int32_t n,
                               int32_t k, int32_t *slot_ids, void *stream);
+
+/* ensure_experts_hybrid (benchmark guide §5.4): the same remap, except that only
+ * the first `take` missing ids (ascending flat id) get slots and are listed for
+ * copy_missing; the rest keep no slot, their entries of slot_ids are -1 (the
+ * expert FFN skips them; they are the CPU executor's share) and they are not
+ * stamped.  take = min(cap, misses, slots not holding a requested id), so a
+ * hybrid step never fails for capacity.  cap = max_fetch when max_fetch >= 0
+ * (hybrid_max_fetch); otherwise misses x min(1, fetch_fraction) rounded half to
+ * even (in double) when fetch_fraction >= 0, where fetch_fraction is the
+ * measured pcie_bw / cpu_bw split; otherwise 1 (no bandwidth profile).
+ * oes_cache_stats reports last_indices (num_indices) and last_missing_full
+ * (num_missing_full).  Errors as oes_ensure_experts, OES_ERR_CAPACITY excepted;
+ * OES_ERR_ARG for a NaN fetch_fraction. */
+oes_status oes_ensure_experts_hybrid(oes_cache *c, int32_t layer, const int32_t *ids, int32_t n,
+                                     int32_t k, int32_t *slot_ids, int32_t max_fetch,
+                                     double fetch_fraction, void *stream);
 
 /* copy_missing: for every (slot, flat id) of the last miss list and every bank
  * b, copy row id % E of layer id / E's host bank b into slot row `slot` of

@@ -63,7 +63,9 @@ class Schema(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_uint64), ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
                 ("evictions", ctypes.c_uint64), ("bytes_copied", ctypes.c_uint64),
-                ("last_misses", ctypes.c_uint32), ("failed_steps", ctypes.c_int32)]
+                ("last_misses", ctypes.c_uint32), ("failed_steps", ctypes.c_int32),
+                ("last_indices", ctypes.c_uint32), ("last_missing_full", ctypes.c_uint32),
+                ("cpu_experts", ctypes.c_uint64)]
 
 
 _lib = None
@@ -96,6 +98,7 @@ _SIGS = {
     "oes_route": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I64, _P]),
     "oes_route_logits": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "oes_ensure_experts": (_I32, [_P, _I32, _P, _I32, _I32, _P, _P]),
+    "oes_ensure_experts_hybrid": (_I32, [_P, _I32, _P, _I32, _I32, _P, _I32, ctypes.c_double, _P]),
     "oes_copy_missing": (_I32, [_P, _P]),
     "oes_expert_ffn_workspace": (_I32, [_P, _I32, _I32, _PI64]),
     "oes_expert_ffn": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P, _I64, _P]),
@@ -282,6 +285,12 @@ class Cache:
     def ensure_experts(self, layer, ids, slot_ids, stream=None):
         n, k = ids.shape
         _check(lib().oes_ensure_experts(self._h, layer, _ptr(ids), n, k, _ptr(slot_ids), _stream(stream)))
+
+    def ensure_experts_hybrid(self, layer, ids, slot_ids, max_fetch=-1, fetch_fraction=-1.0, stream=None):
+        """Hybrid remap: at most the cap of misses get slots; the rest map to -1."""
+        n, k = ids.shape
+        _check(lib().oes_ensure_experts_hybrid(self._h, layer, _ptr(ids), n, k, _ptr(slot_ids), int(max_fetch),
+                                               float(fetch_fraction), _stream(stream)))
 
     def copy_missing(self, stream=None):
         _check(lib().oes_copy_missing(self._h, _stream(stream)))

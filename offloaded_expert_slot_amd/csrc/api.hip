@@ -549,6 +549,9 @@ extern "C" oes_status oes_cache_stats(oes_cache *c, oes_stats *out, void *stream
   out->bytes_copied = ctl.bytes;
   out->last_misses = ctl.last_misses;
   out->failed_steps = ctl.failed_steps;
+  out->last_indices = ctl.last_indices;
+  out->last_missing_full = ctl.last_missing_full;
+  out->cpu_experts = ctl.cpu_experts;
   return OES_OK;
 }
 
@@ -735,8 +738,9 @@ extern "C" oes_status oes_route_logits(const float *logits, int32_t n, int32_t E
 }
 
 // ============================================================================ ensure_experts
-extern "C" oes_status oes_ensure_experts(oes_cache *c, int32_t layer, const int32_t *ids, int32_t n, int32_t k,
-                                         int32_t *slot_ids, void *stream) {
+static oes_status ensure_common(oes_cache *c, int32_t layer, const int32_t *ids, int32_t n, int32_t k,
+                                int32_t *slot_ids, int hybrid, int32_t max_fetch, double fetch_fraction,
+                                void *stream) {
   if (!c) return fail(OES_ERR_ARG, "cache is NULL");
   if (layer < 0 || layer >= c->sc.num_layers) return fail(OES_ERR_ARG, "layer %d outside [0, %d)", layer, c->sc.num_layers);
   if (n < 0 || k < 1) return fail(OES_ERR_ARG, "need n >= 0 and k >= 1");
@@ -757,8 +761,23 @@ extern "C" oes_status oes_ensure_experts(oes_cache *c, int32_t layer, const int3
   a.S = c->S;
   a.Spad = c->Spad;
   a.bpe = c->sc.bytes_per_expert;
+  a.hybrid = hybrid;
+  a.max_fetch = max_fetch;
+  a.fetch_fraction = fetch_fraction;
   HIP_TRY(launch_lru_remap(a, as_stream(stream)));
   return OES_OK;
+}
+
+extern "C" oes_status oes_ensure_experts(oes_cache *c, int32_t layer, const int32_t *ids, int32_t n, int32_t k,
+                                         int32_t *slot_ids, void *stream) {
+  return ensure_common(c, layer, ids, n, k, slot_ids, 0, -1, -1.0, stream);
+}
+
+extern "C" oes_status oes_ensure_experts_hybrid(oes_cache *c, int32_t layer, const int32_t *ids, int32_t n,
+                                                int32_t k, int32_t *slot_ids, int32_t max_fetch,
+                                                double fetch_fraction, void *stream) {
+  if (fetch_fraction != fetch_fraction) return fail(OES_ERR_ARG, "fetch_fraction is NaN");
+  return ensure_common(c, layer, ids, n, k, slot_ids, 1, max_fetch, fetch_fraction, stream);
 }
 
 // ============================================================================ expert FFN

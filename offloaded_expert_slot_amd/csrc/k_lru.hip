@@ -13,6 +13,12 @@
 //            (not empty, stamp, owner, slot) - the i-th miss takes the i-th
 //   |U| > S fails with OES_ERR_CAPACITY and writes nothing to the table
 //   on success clock += 1 and every slot holding a member of U gets the clock.
+// Hybrid steps (FreeToken MoE benchmark guide §5.4, ensure_experts_hybrid): only
+//   the first `take` misses (ascending) are installed, take = min(cap, misses,
+//   slots not holding a member of U); the others keep no slot, their requests
+//   map to -1 (the CPU executor's share) and they are not stamped; no capacity
+//   error.  cap = max_fetch if >= 0, else rint(misses x min(1, fraction)) in
+//   double (round half to even) if fraction >= 0, else 1.
 //
 // Layout in LDS (E <= 4096, S <= 4096):
 //   req[E]   u8   expert e of this layer requested
@@ -24,6 +30,8 @@
 //                      get the all-ones key and sort last.
 // Key encoding: khi = (owner != -1) << 63 | stamp  (stamps < 2^62),
 //               klo = (owner + 1) << 12 | slot     (owner < 2^50, slot < 4096).
+
+#include <math.h>
 
 #include "oes_internal.h"
 
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   }
 
   const bool bad = s_bad != 0;
-  const bool over = nU > S;
+  const bool over = !a.hybrid && nU > S;
   if (bad || over) {
     for (int i = tid; i < a.nk; i += kThreads) a.slot_ids[i] = -1;
     if (tid == 0) {
@@ -312,16 +320,29 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
     return;
   }
 
-  if (nM > 0) {
+  // misses installed this step: all of them, or the hybrid cap
+  int take = nM;
+  if (a.hybrid) {
+    long long cap;
+    if (a.max_fetch >= 0)
+      cap = a.max_fetch;
+    else if (a.fetch_fraction >= 0.0)
+      cap = (long long)rint((double)nM * fmin(1.0, a.fetch_fraction));
+    else
+      cap = 1;
+    const long long avail = (long long)S - (nU - nM);  // slots not holding a member of U
+    take = (int)min(cap, min((long long)nM, avail));
+  }
+  if (take > 0) {
     // 4-5. victim keys ascending (slots holding a member of U sort last): the
-    // first nM of them, by selection for a few misses, else by a full sort
-    if (nM <= kSelectMax) {
+    // first `take` of them, by selection for a few misses, else by a full sort
+    if (take <= kSelectMax) {
       if (a.Spad <= kThreads)
-        select_victims<1>(a, req, base, nM, khi, klo, wmin_h, wmin_l);
+        select_victims<1>(a, req, base, take, khi, klo, wmin_h, wmin_l);
       else if (a.Spad <= 2 * kThreads)
-        select_victims<2>(a, req, base, nM, khi, klo, wmin_h, wmin_l);
+        select_victims<2>(a, req, base, take, khi, klo, wmin_h, wmin_l);
       else
-        select_victims<4>(a, req, base, nM, khi, klo, wmin_h, wmin_l);
+        select_victims<4>(a, req, base, take, khi, klo, wmin_h, wmin_l);
     } else if (a.Spad <= kThreads) {
       sort_victims<1>(a, req, base, khi, klo);
     } else if (a.Spad <= 2 * kThreads) {
@@ -329,10 +350,10 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
     } else {
       sort_victims<4>(a, req, base, khi, klo);
     }
-    // 6. install: the i-th miss takes the i-th victim
+    // 6. install: the i-th miss takes the i-th victim (hybrid: the first `take` misses)
     for (int e = tid; e < E; e += kThreads) {
       const int r = mrank[e];
-      if (r >= 0) {
+      if (r >= 0 && r < take) {
         const int v = (int)(klo[r] & 0xFFFull);
         const int64_t old = a.owner[v];
         if (old != -1) atomicAdd(&s_evict, 1);
@@ -345,22 +366,26 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   }
   __syncthreads();
 
-  // 7. stamp every slot holding a member of U, then the slot map
+  // 7. stamp every slot holding a member of U, then the slot map (hybrid: ids
+  // left without a slot are not stamped and their requests map to -1)
   const uint64_t T = s_clock + 1;
   for (int e = tid; e < E; e += kThreads)
-    if (req[e]) a.stamp[emap[e]] = T;
+    if (req[e] && emap[e] >= 0) a.stamp[emap[e]] = T;
   for (int i = tid; i < a.nk; i += kThreads) a.slot_ids[i] = emap[a.ids[i]];
   if (tid == 0) {
     Ctl *c = a.ctl;
     c->clock = T;
     c->step_ok = 1;
-    c->miss_count = nM;
+    c->miss_count = take;
     c->steps += 1;
     c->hits += (uint64_t)(nU - nM);
-    c->misses += (uint64_t)nM;
+    c->misses += (uint64_t)take;
     c->evictions += (uint64_t)s_evict;
-    c->bytes += (uint64_t)nM * (uint64_t)a.bpe;
-    c->last_misses = (uint32_t)nM;
+    c->bytes += (uint64_t)take * (uint64_t)a.bpe;
+    c->last_misses = (uint32_t)take;
+    c->last_indices = (uint32_t)take;
+    c->last_missing_full = (uint32_t)nM;
+    c->cpu_experts += (uint64_t)(nM - take);
   }
 }
 

@@ -18,6 +18,9 @@ struct Ctl {
   uint64_t steps, hits, misses, evictions, bytes;
   uint32_t last_misses;
   int32_t failed_steps;
+  uint32_t last_indices;       // hybrid: misses fetched by the last step (within the cap)
+  uint32_t last_missing_full;  // hybrid: misses of the last step before the cap
+  uint64_t cpu_experts;        // hybrid: misses left to the CPU executor, summed over steps
 };
 
 // ---------------------------------------------------------------- ensure_experts
@@ -31,6 +34,9 @@ struct LruArgs {
   int32_t *slot_ids;
   int32_t nk, layer, E, S, Spad;
   int64_t bpe;
+  int32_t hybrid;          // 1: ensure_experts_hybrid (fetch cap; overflow requests map to -1)
+  int32_t max_fetch;       // hybrid cap if >= 0
+  double fetch_fraction;   // else the share of the misses to fetch if >= 0, else a cap of one
 };
 hipError_t launch_lru_remap(const LruArgs &a, hipStream_t s);
 // step_ok = 1, miss_count = 0 (a one-thread kernel, safe under graph capture)

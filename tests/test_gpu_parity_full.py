@@ -167,3 +167,43 @@ def test_decode_ffn_batched(name, bs, tokens):
     err = offn.rel_l2(G.bf16_tensor_to_f64(y)[sel], ref)
     print(f"  rel_l2={err:.3e}")
     assert err <= (3e-2 if w.fmt == "nvfp4" else 1e-2)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("max_fetch,frac", [(-1, 0.3), (5, -1.0), (-1, -1.0)])
+def test_hybrid_step_bs8(max_fetch, frac):
+    """ensure_experts_hybrid at full size (bf16 H=2048, every slot foreign): the
+    fetched misses are copied and the FFN runs on the resident pairs only; the
+    overflow pairs map to -1 (the CPU executor's share, not computed here)."""
+    w, hb, c = _setup("bf16_h2048")
+    _case(f"hybrid step bf16 bs=8 max_fetch={max_fetch} frac={frac}")
+    dev = G.dev()
+    bs = 8
+    x = synth.activations(bs, w.H, 0, w.name, step=3).to(dev)
+    wg = synth.router_weight(w.H, w.E, 0, w.name).to(dev)
+    oids, ow, _ = oroute.route(G.bits16(x), G.bits16(wg), w.k)
+    owner, stamp, clock = synth.foreign_state(w.S, w.E)
+    c.set_state(owner, stamp, clock)
+    ids = torch.from_numpy(oids).to(dev)
+    wts = torch.from_numpy(ow.astype(np.float32)).to(dev)
+    slot_ids = torch.empty_like(ids)
+    y = torch.empty((bs, w.H), dtype=torch.int16, device=dev)
+    ws = torch.empty(c.ffn_workspace_bytes(bs, w.k), dtype=torch.uint8, device=dev)
+    c.ensure_experts_hybrid(0, ids, slot_ids, max_fetch, frac)
+    c.copy_missing()
+    c.expert_ffn(x, slot_ids, wts, y, ws)
+    torch.cuda.synchronize()
+    c.check()
+    t = SlotTable(w.S, w.L, w.E)
+    t.set_state(owner, stamp, clock)
+    r = t.ensure_hybrid(0, oids, max_fetch, None if frac < 0 else frac)
+    assert np.array_equal(slot_ids.cpu().numpy(), r.slot_ids)
+    assert c.get_misses() == r.misses
+    st = c.stats()
+    assert (st["last_indices"], st["last_missing_full"]) == (r.num_indices, r.num_missing_full)
+    assert r.num_indices < r.num_missing_full          # the cap bites at this size
+    ref = offn.expert_ffn(w.fmt, w.H, w.I, G.bits16(x), r.slot_ids, ow.astype(np.float32).astype(np.float64),
+                          lambda s: [hb.row(b, int(t.owner[s]) % w.E).numpy() for b in range(len(hb.banks))])
+    err = offn.rel_l2(G.bf16_tensor_to_f64(y), ref)
+    print(f"  fetched {r.num_indices} of {r.num_missing_full} misses, rel_l2={err:.3e}")
+    assert err <= 1e-2

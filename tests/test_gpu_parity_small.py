@@ -4,6 +4,7 @@ Each test prints the case it runs before touching the GPU.  Integer / byte /
 index results must match bit for bit; FFN outputs to the relative-L2 bounds
 (1e-2 for bf16 and fp8 banks, 3e-2 for fp4 banks).
 """
+import os
 import random
 
 import numpy as np
@@ -128,6 +129,81 @@ def test_lru_pool_over_2048_slots():
         rows = 1 if i % 3 else 12          # 8 or 96 routed ids per step
         steps.append((int(rng.integers(L)), rng.integers(0, E, size=(rows, 8)).tolist()))
     _lru_trace(S, L, E, steps, (owner, stamp, 7))
+
+
+def _hybrid_step(c, t, layer, ids_np, max_fetch, frac):
+    d_ids = torch.from_numpy(np.asarray(ids_np, dtype=np.int32)).to(G.dev())
+    d_slots = torch.full(d_ids.shape, -7, dtype=torch.int32, device=G.dev())
+    c.ensure_experts_hybrid(layer, d_ids, d_slots, max_fetch, -1.0 if frac is None else frac)
+    r = t.ensure_hybrid(layer, np.asarray(ids_np), max_fetch, frac)
+    assert c.check_status() == r.status == OK
+    owner, stamp, clock = c.get_state()
+    assert np.array_equal(owner, t.owner) and np.array_equal(stamp, t.stamp) and clock == t.clock
+    assert np.array_equal(d_slots.cpu().numpy(), r.slot_ids)
+    assert c.get_misses() == r.misses
+    st = c.stats()
+    assert (st["last_indices"], st["last_missing_full"]) == (r.num_indices, r.num_missing_full)
+    return r
+
+
+def test_lru_hybrid_hand_trace():
+    """The hand-worked hybrid trace (tests/golden/lru_hybrid_trace_s3_e4.txt) on the device."""
+    _case("lru hybrid hand trace S=3 L=2 E=4")
+    c = G.make_cache("bf16", 2, 4, 64, 64, 3, {})
+    t = SlotTable(3, 2, 4)
+    lines = [l.split("#")[0].strip() for l in open(os.path.join(os.path.dirname(__file__), "golden",
+                                                                 "lru_hybrid_trace_s3_e4.txt"))]
+    for line in [l for l in lines if l.startswith("step")]:
+        _, layer, ids, mf, frac = line.split("->")[0].split()
+        rows = [[int(v) for v in r.split(",")] for r in ids.split(";")]
+        _hybrid_step(c, t, int(layer), rows, int(mf), None if frac == "-" else float(frac))
+    assert c.stats()["cpu_experts"] == 2 + 1 + 1 + 1 + 1 + 0 + 1
+
+
+def test_lru_hybrid_random_traces():
+    rng = random.Random(17)
+    for trial in range(6):
+        L, E, S = rng.randint(1, 3), rng.randint(3, 40), rng.randint(1, 24)
+        _case(f"lru hybrid random trial={trial} L={L} E={E} S={S}")
+        c = G.make_cache("bf16", L, E, 64, 64, S, {})
+        t = SlotTable(S, L, E)
+        for _ in range(30):
+            n, k = rng.randint(1, 4), rng.randint(1, 6)
+            ids = [[rng.randrange(E) for _ in range(k)] for _ in range(n)]
+            _hybrid_step(c, t, rng.randrange(L), ids, rng.choice([-1, 0, 1, 3, 100]),
+                         rng.choice([None, 0.0, 0.3, 0.5, 1.0, 1.5]))
+            if rng.random() < 0.3:                       # interleave plain steps
+                layer = rng.randrange(L)
+                ids = np.array([[rng.randrange(E) for _ in range(2)]], dtype=np.int32)
+                d = torch.from_numpy(ids).to(G.dev())
+                ds = torch.empty_like(d)
+                c.ensure_experts(layer, d, ds)
+                r = t.ensure(layer, ids)
+                assert c.check_status() == r.status
+
+
+def test_hybrid_copy_moves_only_fetched_rows():
+    fmt, L, E, H, I, S = "bf16", 1, 16, 256, 128, 8
+    _case("hybrid copy: fetched rows only")
+    banks = {0: G.make_banks(fmt, E, H, I, tag="hyb")}
+    c = G.make_cache(fmt, L, E, H, I, S, banks)
+    host = G.oracle_host(banks, L, len(banks[0].banks))
+    t = SlotTable(S, L, E)
+    c.fill_slots(0x5A)
+    ids = [[3, 9, 1, 12], [7, 3, 14, 0]]                 # 7 distinct, all missing
+    r = _hybrid_step(c, t, 0, ids, -1, 0.4)             # cap round(7 * 0.4) = 3
+    assert r.num_indices == 3 and r.num_missing_full == 7 and r.overflow == [7, 9, 12, 14]
+    c.copy_missing()
+    torch.cuda.synchronize()
+    c.check()
+    fetched = {s for s, _ in r.misses}
+    for b in range(len(host)):
+        view = c.slot_bank_view(b)
+        for s, fid in r.misses:
+            assert np.array_equal(view[s].cpu().numpy(), host[b][0][fid])
+        for s in range(S):
+            if s not in fetched:
+                assert bool((view[s] == 0x5A).all()), (b, s)
 
 
 def test_lru_capacity_and_bad_ids_leave_state():
