@@ -81,6 +81,23 @@ def fp4x2_unpack(packed):
     return out
 
 
+def q4x2_unpack(packed):
+    """GGUF Q4_0 code bytes -> 4-bit codes in element order, along the last axis.
+
+    GGUF block_q4_0: 32 elements per block; of the block's 16 code bytes, byte j
+    holds element j in its low nibble and element j + 16 in its high nibble.
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    blocks = p.reshape(p.shape[:-1] + (p.shape[-1] // 16, 16))
+    codes = np.concatenate([blocks & 0xF, blocks >> 4], axis=-1)       # [..., blocks, 32]
+    return codes.reshape(p.shape[:-1] + (2 * p.shape[-1],))
+
+
+def q4_0(codes):
+    """GGUF Q4_0 4-bit codes -> the integers q - 8 (the weight before its block scale d)."""
+    return np.asarray(codes).astype(np.int64).astype(np.float64) - 8.0
+
+
 def via_table(fn, codes, ncodes):
     """fn applied to integer codes by evaluating fn once on every possible code.
 

@@ -19,6 +19,7 @@ Dequantisation (readings; formats from the pages' bank list):
   nvfp4       W[r, c] = e2m1(code[r, c]) * e4m3(scale[r, c // 16]) * fp16(global[r])
   mxfp4 (T)   W[n, c] = e2m1(code of blocks[c // 32, n, (c % 32) // 2], nibble c % 2)
                         * 2 ** (scales[c // 32, n] - 127), plus a bf16 bias per output
+  q4_0        W[r, c] = (q[r, c] - 8) * fp16(d[r, c // 32]), q unpacked in GGUF block order
 
 Everything is float64.  A slot id of -1 contributes nothing (reserved for
 experts computed elsewhere).
@@ -66,6 +67,13 @@ def _mxfp4_matrix(raw_b, bshape, raw_s, sshape):
     return vals.transpose(1, 0, 2).reshape(n, kb * 32)
 
 
+def _q4_0_matrix(raw_q, qshape, raw_d, dshape):
+    rows, half = qshape
+    vals = decode.q4_0(decode.q4x2_unpack(raw_q.reshape(rows, half)))   # [rows, K]
+    d = decode.fp16(raw_d.view(np.uint16).reshape(dshape))               # [rows, K/32]
+    return vals * np.repeat(d, 32, axis=1)
+
+
 def dequant_expert(fmt, hidden, inter, bank_rows):
     """One expert's rows (one uint8 array per bank, schema order) -> (Wgu, Wd, b_gu, b_d) in float64."""
     specs = schema.bank_specs(fmt, hidden, inter)
@@ -101,6 +109,12 @@ def dequant_expert(fmt, hidden, inter, bank_rows):
         wgu, wd = _mxfp4_matrix(rb1, b1, rs1, ss1), _mxfp4_matrix(rb2, b2, rs2, ss2)
         bgu = decode.bf16(rbias1.view(np.uint16))
         bd = decode.bf16(rbias2.view(np.uint16))
+    elif fmt == schema.Q4_0:
+        _, q1, rq1 = _rows(bank_rows, "gate_up_q", specs)
+        _, d1, rd1 = _rows(bank_rows, "gate_up_d", specs)
+        _, q2, rq2 = _rows(bank_rows, "down_q", specs)
+        _, d2, rd2 = _rows(bank_rows, "down_d", specs)
+        wgu, wd = _q4_0_matrix(rq1, q1, rd1, d1), _q4_0_matrix(rq2, q2, rd2, d2)
     else:
         raise ValueError(fmt)
     if wgu.shape != (2 * inter, hidden) or wd.shape != (hidden, inter):

@@ -9,7 +9,10 @@ block, an fp16 global per output row, for gate_up and for down); the MXFP4
 format is six transposed banks (_blocks, _scales, _bias for each matrix).  The
 FP8 block format (e4m3 weights with fp32 scales per 128x128 block) is listed on
 the architecture page; its bank split (weights and scales as separate banks)
-is the reading taken here.
+is the reading taken here.  GGUF Q4_0 is the fifth format the architecture page
+lists; its values follow the published GGUF block_q4_0 definition (32 weights
+share one fp16 scale d, weight = (q - 8) * d) and its bank split - the 4-bit
+codes and the fp16 scales as separate banks, as for NVFP4 - is a reading.
 
 Weights use the [out, in] convention: gate_up is [2I, H] and down is [H, I].
 Rows [0, I) of gate_up are the gate projection, rows [I, 2I) the up
@@ -17,11 +20,12 @@ projection (a reading: the pages do not say).
 
 Each entry is (name, element tag, row shape, row bytes).  The element tag says
 how to read a row: "bf16", "e4m3", "f32", "fp4x2" (two e2m1 codes per byte),
-"fp16", "e8m0", "u8".
+"fp16", "e8m0", "u8", "q4x2" (GGUF Q4_0 codes: in every 16 bytes, byte j holds
+element j in its low nibble and element j + 16 in its high nibble).
 """
 
-BF16, FP8_BLOCK128, NVFP4, MXFP4_T = "bf16", "fp8_block128", "nvfp4", "mxfp4_t"
-FORMATS = (BF16, FP8_BLOCK128, NVFP4, MXFP4_T)
+BF16, FP8_BLOCK128, NVFP4, MXFP4_T, Q4_0 = "bf16", "fp8_block128", "nvfp4", "mxfp4_t", "q4_0"
+FORMATS = (BF16, FP8_BLOCK128, NVFP4, MXFP4_T, Q4_0)
 
 _ELEM_BYTES = {"bf16": 2, "e4m3": 1, "f32": 4, "fp16": 2, "e8m0": 1, "u8": 1}
 
@@ -30,7 +34,7 @@ def _bytes(elem, shape):
     n = 1
     for d in shape:
         n *= d
-    if elem == "fp4x2":
+    if elem in ("fp4x2", "q4x2"):
         return n  # shape already counts bytes (two codes per byte)
     return n * _ELEM_BYTES[elem]
 
@@ -68,6 +72,13 @@ def bank_specs(fmt: str, hidden: int, inter: int):
                  ("down_blocks", "u8", (I // 32, H, 16)),
                  ("down_scales", "e8m0", (I // 32, H)),
                  ("down_bias", "bf16", (H,))]
+    elif fmt == Q4_0:
+        if H % 32 or I % 32:
+            raise ValueError("q4_0 needs H and I divisible by 32")
+        banks = [("gate_up_q", "q4x2", (2 * I, H // 2)),
+                 ("gate_up_d", "fp16", (2 * I, H // 32)),
+                 ("down_q", "q4x2", (H, I // 2)),
+                 ("down_d", "fp16", (H, I // 32))]
     else:
         raise ValueError(f"unknown format {fmt!r}")
     return [(name, elem, shape, _bytes(elem, shape)) for name, elem, shape in banks]

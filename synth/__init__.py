@@ -108,6 +108,20 @@ def mxfp4_t_encode(w):
     return codes.permute(1, 0, 2).contiguous(), e.to(torch.uint8).t().contiguous()
 
 
+def q4_0_encode(w):
+    """[R, K] float32 (K % 32 == 0) -> (codes uint8 [R, K/2] in GGUF block order, d fp16 bits int16 [R, K/32]).
+
+    d = amax / 7 of each 32-block (fp16), q = clip(round(w / d) + 8, 0, 15);
+    byte j of a block holds q[j] (low nibble) and q[j + 16] (high nibble).
+    """
+    R, K = w.shape
+    blk = w.reshape(R, K // 32, 32)
+    d = (torch.clamp(blk.abs().amax(dim=2), min=1e-6) / 7.0).to(torch.float16)
+    q = (torch.round(blk / d.to(torch.float32)[:, :, None]) + 8).clamp(0, 15).to(torch.uint8)
+    codes = q[..., :16] | (q[..., 16:] << 4)
+    return codes.reshape(R, K // 2), d.view(torch.int16)
+
+
 # ----------------------------------------------------------------------------- experts
 def expert_weights(fmt, hidden, inter, seed, tag, flat_id, device="cpu"):
     """float32 draws (Wgu [2I, H], Wd [H, I], b_gu [2I] or None, b_d [H] or None) of one expert."""
@@ -132,6 +146,10 @@ def encode_expert(fmt, wgu, wd, bgu=None, bd=None):
         c1, s1, g1 = nvfp4_encode(wgu)
         c2, s2, g2 = nvfp4_encode(wd)
         return [_u8(c1), _u8(s1), _u8(g1), _u8(c2), _u8(s2), _u8(g2)]
+    if fmt == "q4_0":
+        q1, d1 = q4_0_encode(wgu)
+        q2, d2 = q4_0_encode(wd)
+        return [_u8(q1), _u8(d1), _u8(q2), _u8(d2)]
     if fmt == "mxfp4_t":
         b1, s1 = mxfp4_t_encode(wgu)
         b2, s2 = mxfp4_t_encode(wd)

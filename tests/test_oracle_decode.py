@@ -1,4 +1,6 @@
 """Pins of the oracle's bit-field decoders against library conversions and the OCP tables."""
+import os
+
 import numpy as np
 import torch
 
@@ -74,3 +76,23 @@ def test_table_evaluation_equals_direct():
         _same(decode.via_table(fn, b, n), fn(b))
     c = rng.integers(0, 16, size=(5, 9))
     _same(decode.via_table(decode.e2m1, c, 16), decode.e2m1(c))
+
+
+def test_q4_0_golden_block():
+    """A GGUF Q4_0 block worked by hand (tests/golden/q4_0_block.txt)."""
+    lines = [l.split("#")[0].split() for l in open(os.path.join(os.path.dirname(__file__), "golden", "q4_0_block.txt"))]
+    kv = {l[0]: l[1:] for l in lines if l}
+    d = decode.fp16(np.array([int(kv["d_bits"][0], 16)], dtype=np.uint16))[0]
+    codes = np.array([int(b, 16) for b in kv["bytes"]], dtype=np.uint8)
+    got = decode.q4_0(decode.q4x2_unpack(codes)) * d
+    assert got.tolist() == [float(v) for v in kv["values"]]
+
+
+def test_q4x2_unpack_blocks_are_independent():
+    rng = np.random.default_rng(3)
+    a = rng.integers(0, 256, size=(5, 64), dtype=np.uint8)          # 4 blocks per row
+    whole = decode.q4x2_unpack(a)
+    for b in range(4):
+        assert np.array_equal(whole[:, 32 * b:32 * b + 32], decode.q4x2_unpack(a[:, 16 * b:16 * b + 16]))
+    # element j + 16 of a block is the high nibble of byte j, not of byte 2j or 2j+1
+    assert np.array_equal(whole[:, 16:32], a[:, :16] >> 4)

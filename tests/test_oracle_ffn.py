@@ -64,6 +64,7 @@ def test_bf16_weighted_combine_equals_dense():
     ("fp8_block128", 256, 128, 0.05),
     ("nvfp4", 64, 32, 0.15),
     ("mxfp4_t", 64, 64, 0.2),
+    ("q4_0", 256, 128, 0.15),
 ])
 def test_dequant_round_trip(fmt, H, I, bound):
     wgu, wd, bgu, bd = synth.expert_weights(fmt, H, I, 0, "rt", 11)
@@ -104,6 +105,25 @@ def test_nvfp4_dequant_structure():
             rows.append(np.frombuffer(np.full(nbytes // 2, 1.0, dtype=np.float16).tobytes(), dtype=np.uint8))
     dg, dd, _, _ = ffn.dequant_expert("nvfp4", H, I, rows)
     assert (dg == 1.0).all() and (dd == 1.0).all()
+
+
+def test_q4_0_dequant_structure():
+    # codes 0x99 (q = 9 -> +1) with d = fp16 0.25 -> every weight 0.25; codes 0x88 -> 0
+    H, I = 64, 32
+    for byte, want in ((0x99, 0.25), (0x88, 0.0), (0x70, None)):
+        rows = []
+        for name, elem, shape, nbytes in schema.bank_specs("q4_0", H, I):
+            if name.endswith("_q"):
+                rows.append(np.full(nbytes, byte, dtype=np.uint8))
+            else:
+                rows.append(np.frombuffer(np.full(nbytes // 2, 0.25, dtype=np.float16).tobytes(), dtype=np.uint8))
+        dg, dd, _, _ = ffn.dequant_expert("q4_0", H, I, rows)
+        if want is not None:
+            assert (dg == want).all() and (dd == want).all()
+        else:
+            # 0x70: low nibble 0 -> -8 * 0.25 for the first 16 of every 32, high nibble 7 -> -0.25
+            blk = dg.reshape(2 * I, H // 32, 32)
+            assert (blk[:, :, :16] == -2.0).all() and (blk[:, :, 16:] == -0.25).all()
 
 
 @pytest.mark.parametrize("fmt,H,I", [("bf16", 32, 16), ("mxfp4_t", 64, 32)])

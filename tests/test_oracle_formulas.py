@@ -45,6 +45,7 @@ def test_round_half_even_reading():
     ("fp8_block128", 4096, 1536, 18878976, [12582912, 3072, 6291456, 1536]),
     ("nvfp4", 7168, 2048, 24795136, [14680064, 1835008, 8192, 7340032, 917504, 14336]),
     ("mxfp4_t", 2880, 2880, 13236480, [8294400, 518400, 11520, 4147200, 259200, 5760]),
+    ("q4_0", 2048, 768, 2654208, [1572864, 196608, 786432, 98304]),
 ])
 def test_bank_bytes(fmt, H, I, bpe, banks):
     specs = schema.bank_specs(fmt, H, I)
