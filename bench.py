@@ -20,7 +20,8 @@ Also printed (same JSON line): the copy sweep of the benchmark guide's columns
 25 event-timed ensure+copy repeats, fused and per-bank), decode tok/s at every
 miss rate, the measured ceilings (pinned H2D by DMA and by the zero-copy
 kernel, HBM streaming read, bf16 MFMA loop), the roofline of the dominant kernel and of the
-FFN, the MXFP4 prefill layer (grouped FFN on MFMA, whole-layer stream, the
+FFN, the cold decode FFN of every decode bank format (bf16, fp8 block, nvfp4,
+GGUF Q4_0) at its workload's shape, the MXFP4 prefill layer (grouped FFN on MFMA, whole-layer stream, the
 overlapped loop over 4 layers) and the CPU oracle timed on this host.
 """
 import argparse
@@ -226,6 +227,8 @@ def main():
     ffn_bytes = w.k * bpe
     log("ffn", {"launches": n_ffn, "slot_maps": nsets, "ms_per_launch": round(ffn_alone_ms, 5)})
 
+    ffn_formats = _ffn_formats(WORKLOADS, nsets, n_ffn, probes, log)
+
     # ---------------------------------------------------------------- copy sweep
     sweep = []
     if not args.no_sweep:
@@ -316,10 +319,59 @@ def main():
                    "misses": head["misses"], "active": active, "bytes_per_expert": bpe},
         "tok_ms": head["tok_ms"], "copy_GBps": head.get("copy_GBps"),
         "roofline": roof, "kernels": kernels, "probes": probes, "decode_per_miss_rate": per_mr,
-        "copy_sweep": sweep, "prefill": prefill, "cpu_baseline": cpu,
+        "copy_sweep": sweep, "ffn_formats": ffn_formats, "prefill": prefill, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     cache.close()
+
+
+def _ffn_formats(workloads, nsets, launches, probes, log):
+    """Decode FFN (bs=1, top-k) of every decode bank format at its workload's
+    shape, timed cold like the headline's: back-to-back launches over `nsets`
+    slot maps of k distinct slots each.  Slot bytes are a constant fill (finite
+    values of every element type); they do not change the time."""
+    import numpy as np
+    import torch
+
+    import offloaded_expert_slot_amd as oes
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("bf16_h2048", "fp8_h4096", "nvfp4_h7168", "q4_0_h2048"):
+        w = workloads[name]
+        sc = oes.schema_make(w.fmt, w.L, w.E, w.H, w.I)
+        slots = nsets * w.k
+        c = oes.Cache(sc, slots, 0)
+        c.fill_slots(0x11)
+        x = synth.activations(1, w.H, 0, w.name).to(dev)
+        wts = torch.full((1, w.k), 1.0 / w.k, dtype=torch.float32, device=dev)
+        y = torch.empty((1, w.H), dtype=torch.int16, device=dev)
+        ws = torch.empty(c.ffn_workspace_bytes(1, w.k), dtype=torch.uint8, device=dev)
+        perm = np.random.default_rng(1).permutation(slots).astype(np.int32)
+        maps = [torch.from_numpy(perm[i * w.k:(i + 1) * w.k].reshape(1, w.k).copy()).to(dev) for i in range(nsets)]
+        for i in range(4):
+            c.expert_ffn(x, maps[i], wts, y, ws)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(launches):
+            c.expert_ffn(x, maps[i % nsets], wts, y, ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        c.check()
+        ms = a.elapsed_time(b) / launches
+        nbytes = w.k * sc.bytes_per_expert
+        row = {"format": w.fmt, "hidden": w.H, "inter": w.I, "topk": w.k, "bytes_per_launch": nbytes,
+               "avg_ms": ms, "GBps": nbytes / (ms * 1e6), "frac_of_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS}
+        if probes:
+            row["frac_of_measured_hbm_read"] = row["GBps"] / probes["hbm_read_GBps"]
+        out[name] = row
+        log("ffn format", {k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()})
+        c.close()
+        del x, y, ws, maps
+    torch.cuda.empty_cache()
+    return out
 
 
 def _pmc_traffic(kernel):

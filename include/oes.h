@@ -76,11 +76,16 @@ int32_t oes_abi_version(void);
  *                     16 bytes), gate_up_scales [H/32,2I] e8m0, gate_up_bias
  *                     [2I] bf16, then the same three for down over [I/32,H,16]
  *                     (W[n,c] = e2m1 * 2^(scale-127); bias added after the matmul)
+ *   OES_Q4_0          gate_up_q [2I,H/2] (GGUF block_q4_0 codes: in every 16
+ *                     bytes, byte j holds element j in its low nibble and
+ *                     element j+16 in its high nibble), gate_up_d [2I,H/32] fp16,
+ *                     down_q [H,I/2], down_d [H,I/32] (W = (q - 8) * d of its
+ *                     32-block; the fifth format of architecture walk-through §5)
  */
-enum { OES_BF16 = 0, OES_FP8_BLOCK128 = 1, OES_NVFP4 = 2, OES_MXFP4_T = 3 };
+enum { OES_BF16 = 0, OES_FP8_BLOCK128 = 1, OES_NVFP4 = 2, OES_MXFP4_T = 3, OES_Q4_0 = 4 };
 enum {
   OES_ELEM_BF16 = 0, OES_ELEM_E4M3 = 1, OES_ELEM_F32 = 2, OES_ELEM_FP4X2 = 3,
-  OES_ELEM_FP16 = 4, OES_ELEM_E8M0 = 5, OES_ELEM_U8 = 6
+  OES_ELEM_FP16 = 4, OES_ELEM_E8M0 = 5, OES_ELEM_U8 = 6, OES_ELEM_Q4X2 = 7
 };
 #define OES_MAX_BANKS 6
 #define OES_MAX_SLOTS 4096     /* slot pool limit of the single-workgroup remap */
@@ -281,7 +286,7 @@ oes_status oes_expert_ffn_workspace(const oes_cache *c, int32_t n, int32_t k, in
  * in registers; sums are fp32; y is bf16 (round to nearest even).
  *   x [n, H] bf16 device, slot_ids [n, k] int32 device (-1 = skip the pair),
  *   w [n, k] float device, y [n, H] bf16 device out, workspace device.
- * Formats: OES_BF16, OES_FP8_BLOCK128, OES_NVFP4 (decode).  Limits:
+ * Formats: OES_BF16, OES_FP8_BLOCK128, OES_NVFP4, OES_Q4_0 (decode).  Limits:
  * n * k <= 65536, k <= 32.  A no-op when the last ensure_experts failed on the
  * device.  Async. */
 oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
@@ -345,9 +350,11 @@ oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *
 
 /* ------------------------------------------------------------------ decoder check */
 /* Decode `n` elements of type `elem` (OES_ELEM_E4M3, OES_ELEM_FP4X2,
- * OES_ELEM_E8M0, OES_ELEM_BF16, OES_ELEM_FP16) from device `codes` into device
- * float `out` with the same device routines the FFN kernels use (FP4X2: two
- * elements per byte, element 2j in the low nibble).  Async.  For tests. */
+ * OES_ELEM_E8M0, OES_ELEM_BF16, OES_ELEM_FP16, OES_ELEM_Q4X2) from device
+ * `codes` into device float `out` with the same device routines the FFN
+ * kernels use (FP4X2: two elements per byte, element 2j in the low nibble;
+ * Q4X2: n a multiple of 32, GGUF Q4_0 nibble order, output q - 8 before the
+ * block scale).  Async.  For tests. */
 oes_status oes_debug_decode(int32_t elem, const void *codes, int32_t n, float *out, void *stream);
 
 #ifdef __cplusplus

@@ -24,9 +24,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboes.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "oes.h")
 
-BF16, FP8_BLOCK128, NVFP4, MXFP4_T = 0, 1, 2, 3
-FORMAT_IDS = {"bf16": BF16, "fp8_block128": FP8_BLOCK128, "nvfp4": NVFP4, "mxfp4_t": MXFP4_T}
-ELEM_BF16, ELEM_E4M3, ELEM_F32, ELEM_FP4X2, ELEM_FP16, ELEM_E8M0, ELEM_U8 = range(7)
+BF16, FP8_BLOCK128, NVFP4, MXFP4_T, Q4_0 = 0, 1, 2, 3, 4
+FORMAT_IDS = {"bf16": BF16, "fp8_block128": FP8_BLOCK128, "nvfp4": NVFP4, "mxfp4_t": MXFP4_T, "q4_0": Q4_0}
+ELEM_BF16, ELEM_E4M3, ELEM_F32, ELEM_FP4X2, ELEM_FP16, ELEM_E8M0, ELEM_U8, ELEM_Q4X2 = range(8)
 OPT_FUSED_COPY, OPT_COPY_MODE, OPT_COPY_BLOCKS = 1, 2, 3
 COPY_ZERO, COPY_SDMA = 0, 1
 OK, ERR_ARG, ERR_CAPACITY, ERR_HIP, ERR_NOMEM, ERR_STATE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6

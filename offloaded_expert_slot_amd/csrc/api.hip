@@ -252,6 +252,14 @@ extern "C" oes_status oes_schema_make(int32_t format, int32_t L, int32_t E, int3
       set_spec(&sc.bank[4], "down_scales", OES_ELEM_E8M0, 2, i / 32, h, 0, (i / 32) * h);
       set_spec(&sc.bank[5], "down_bias", OES_ELEM_BF16, 1, h, 0, 0, h * 2);
       break;
+    case OES_Q4_0:
+      if (H % 32 || I % 32) return fail(OES_ERR_ARG, "q4_0 needs H and I multiples of 32");
+      sc.num_banks = 4;
+      set_spec(&sc.bank[0], "gate_up_q", OES_ELEM_Q4X2, 2, i2, h / 2, 0, i2 * h / 2);
+      set_spec(&sc.bank[1], "gate_up_d", OES_ELEM_FP16, 2, i2, h / 32, 0, i2 * (h / 32) * 2);
+      set_spec(&sc.bank[2], "down_q", OES_ELEM_Q4X2, 2, h, i / 2, 0, h * i / 2);
+      set_spec(&sc.bank[3], "down_d", OES_ELEM_FP16, 2, h, i / 32, 0, h * (i / 32) * 2);
+      break;
     default:
       return fail(OES_ERR_ARG, "unknown format %d", format);
   }
@@ -1048,8 +1056,10 @@ extern "C" oes_status oes_debug_decode(int32_t elem, const void *codes, int32_t 
   if (n == 0) return OES_OK;
   if (!codes || !out) return fail(OES_ERR_ARG, "NULL buffer");
   if (elem != OES_ELEM_E4M3 && elem != OES_ELEM_FP4X2 && elem != OES_ELEM_E8M0 && elem != OES_ELEM_BF16 &&
-      elem != OES_ELEM_FP16)
+      elem != OES_ELEM_FP16 && elem != OES_ELEM_Q4X2)
     return fail(OES_ERR_ARG, "unsupported element type %d", elem);
+  if (elem == OES_ELEM_Q4X2 && n % 32)
+    return fail(OES_ERR_ARG, "q4x2 codes come in blocks of 32 elements (n = %d)", n);
   HIP_TRY(launch_debug_decode(elem, static_cast<const uint8_t *>(codes), n, out, as_stream(stream)));
   return OES_OK;
 }

@@ -14,8 +14,12 @@
 // Weights are turned into bf16 pairs in registers - exactly, since e4m3 and
 // e2m1 values are bf16 numbers - and multiplied with bf16 operands held in LDS
 // by v_dot2_f32_bf16 (fp32 accumulation).  Per-block scales (fp8: one fp32 per
-// 128x128 block; nvfp4: one e4m3 per 16 elements) multiply the partial sums;
-// the nvfp4 per-row fp16 global multiplies the finished row sum.  Lane sums are
+// 128x128 block; nvfp4: one e4m3 per 16 elements; q4_0: one fp16 per 32)
+// multiply the partial sums; the nvfp4 per-row fp16 global multiplies the
+// finished row sum.  A GGUF Q4_0 code q becomes the exact bf16 value 128 + q by
+// byte permutation (0x43 is the high byte of bf16 128, whose unit step is 1);
+// the dot product of a block then starts from -136 * (sum of its 32 operand
+// values), which makes every element count as q - 8.  Lane sums are
 // reduced with cross-lane shuffles.  h is kept as bf16 between the kernels.
 // y is bf16, rounded to nearest even.
 
@@ -65,12 +69,27 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 }
 __device__ inline float fp16_to_f32(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
 
+// bytes 2P and 2P + 1 of n (each a 4-bit code q) -> packed bf16 pair (128 + q_lo, 128 + q_hi)
+template <int P>
+__device__ inline uint32_t q4_pair_bf16(uint32_t n) {
+  // v_perm: selector bytes 0..3 pick bytes of the second operand, 4..7 of the first
+  return __builtin_amdgcn_perm(0x43434343u, n, P ? 0x04030402u : 0x04010400u);
+}
+// sum of the 8 bf16 values in x (fp32)
+__device__ inline float sum8_bf16(const u32x4 x, float acc) {
+  constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
+  acc = dot2(x.x, kOnes, acc);
+  acc = dot2(x.y, kOnes, acc);
+  acc = dot2(x.z, kOnes, acc);
+  return dot2(x.w, kOnes, acc);
+}
+
 // ------------------------------------------------------------------ matrix views
 // One matrix (gate_up or down) of the slot banks, for every slot.
 struct Mat {
   const uint8_t *codes;   // slot s, row r at codes + s*codes_slot + r*row_bytes
   int64_t codes_slot, row_bytes;
-  const uint8_t *scale;   // fp8: f32 [rows/128][K/128]; nvfp4: e4m3 [rows][K/16]
+  const uint8_t *scale;   // fp8: f32 [rows/128][K/128]; nvfp4: e4m3 [rows][K/16]; q4_0: fp16 [rows][K/32]
   int64_t scale_slot;
   int32_t scale_ld;
   const uint8_t *glob;    // nvfp4: fp16 [rows]
@@ -100,7 +119,7 @@ __device__ inline void load_row(RowRegs &R, const Mat &m, int slot, int row, int
       if (FMT == OES_FP8_BLOCK128) {
         const float *s = reinterpret_cast<const float *>(m.scale + (int64_t)slot * m.scale_slot);
         R.sc[q] = __float_as_uint(s[(row >> 7) * m.scale_ld + (c >> 3)]);
-      } else if (FMT == OES_NVFP4) {
+      } else if (FMT == OES_NVFP4 || FMT == OES_Q4_0) {  // 16 bits per chunk
         const uint16_t *s = reinterpret_cast<const uint16_t *>(m.scale + (int64_t)slot * m.scale_slot +
                                                                (int64_t)row * m.scale_ld);
         R.sc[q] = s[c];
@@ -110,10 +129,11 @@ __device__ inline void load_row(RowRegs &R, const Mat &m, int slot, int row, int
 }
 
 // Dot product of one 16-byte weight chunk (EPC elements) with its bf16 operand
-// (EPC/8 16-byte vectors at xo, in LDS or registers); fp8 / nvfp4 block scales
-// (packed in sc) are applied here.
+// (EPC/8 16-byte vectors at xo, in LDS or registers); fp8 / nvfp4 / q4_0 block
+// scales (packed in sc) are applied here.  xsum (q4_0 only) is the sum of the
+// chunk's 32 operand values.
 template <int FMT>
-__device__ inline float dot_chunk(const u32x4 w, uint32_t sc, const u32x4 *xo) {
+__device__ inline float dot_chunk(const u32x4 w, uint32_t sc, const u32x4 *xo, float xsum = 0.f) {
   if (FMT == OES_BF16) {
     const u32x4 x = xo[0];
     float acc = 0.f;
@@ -134,6 +154,22 @@ __device__ inline float dot_chunk(const u32x4 w, uint32_t sc, const u32x4 *xo) {
     s = dot2(fp8_pair_bf16<false>(w.w), x1.z, s);
     s = dot2(fp8_pair_bf16<true>(w.w), x1.w, s);
     return s * __uint_as_float(sc);
+  } else if (FMT == OES_Q4_0) {
+    // one GGUF block: byte j holds element j (low nibble) and element j + 16 (high)
+    const u32x4 x0 = xo[0], x1 = xo[1], x2 = xo[2], x3 = xo[3];
+    const uint32_t xl[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const uint32_t xh[8] = {x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    float s = -136.f * xsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = wv[i] & 0x0f0f0f0fu, hi = (wv[i] >> 4) & 0x0f0f0f0fu;
+      s = dot2(q4_pair_bf16<0>(lo), xl[2 * i], s);
+      s = dot2(q4_pair_bf16<1>(lo), xl[2 * i + 1], s);
+      s = dot2(q4_pair_bf16<0>(hi), xh[2 * i], s);
+      s = dot2(q4_pair_bf16<1>(hi), xh[2 * i + 1], s);
+    }
+    return s * fp16_to_f32((uint16_t)sc);
   } else {  // NVFP4: 32 elements, two 16-element scale blocks
     const u32x4 x0 = xo[0], x1 = xo[1], x2 = xo[2], x3 = xo[3];
     float s0 = 0.f, s1 = 0.f;
@@ -166,17 +202,21 @@ template <>
 struct Epc<OES_FP8_BLOCK128> { static constexpr int v = 16; };
 template <>
 struct Epc<OES_NVFP4> { static constexpr int v = 32; };
+template <>
+struct Epc<OES_Q4_0> { static constexpr int v = 32; };
 
-// Partial dot product of this lane's chunks of a row with a bf16 operand vector in LDS.
+// Partial dot product of this lane's chunks of a row with a bf16 operand vector in
+// LDS (op; q4_0: opsum holds the operand's per-chunk sums).
 template <int FMT, int G>
-__device__ inline float dot_row(const RowRegs &R, const uint16_t *op, int lg, int q0, int nq) {
+__device__ inline float dot_row(const RowRegs &R, const uint16_t *op, const float *opsum, int lg, int q0, int nq) {
   constexpr int EPC = Epc<FMT>::v;
   float acc = 0.f;
 #pragma unroll
   for (int q = 0; q < kMaxQ; ++q) {
     if (q < nq) {
       const int c = (q0 + q) * G + lg;
-      acc += dot_chunk<FMT>(R.w[q], R.sc[q], reinterpret_cast<const u32x4 *>(op + c * EPC));
+      const float xs = FMT == OES_Q4_0 ? opsum[c] : 0.f;
+      acc += dot_chunk<FMT>(R.w[q], R.sc[q], reinterpret_cast<const u32x4 *>(op + c * EPC), xs);
     }
   }
   return acc;
@@ -250,6 +290,17 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
   const int t = p / a.k;
   stage_bf16(xs, a.x + (int64_t)t * a.H, a.H);
   __syncthreads();
+  float *xsums = reinterpret_cast<float *>(xs + a.H);  // q4_0: sum of every 32-element block of x
+  if (FMT == OES_Q4_0) {
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(xs);
+    for (int b = threadIdx.x; b < a.H / 32; b += kThreads) {
+      float acc = 0.f;
+#pragma unroll
+      for (int o = 0; o < 4; ++o) acc = sum8_bf16(xv[4 * b + o], acc);
+      xsums[b] = acc;
+    }
+    __syncthreads();
+  }
   constexpr int NSG = kThreads / G;
   const int sg = threadIdx.x / G, lg = threadIdx.x % G;
   const int r = blockIdx.x * NSG + sg;
@@ -261,8 +312,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
     RowRegs Rg, Ru;
     load_row<FMT, G>(Rg, m, slot, r, lg, q0, nq);
     load_row<FMT, G>(Ru, m, slot, a.I + r, lg, q0, nq);
-    g += dot_row<FMT, G>(Rg, xs, lg, q0, nq);
-    u += dot_row<FMT, G>(Ru, xs, lg, q0, nq);
+    g += dot_row<FMT, G>(Rg, xs, xsums, lg, q0, nq);
+    u += dot_row<FMT, G>(Ru, xs, xsums, lg, q0, nq);
     gg = Rg.gl;
     gu = Ru.gl;
   }
@@ -322,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int lrb) {
   const uint32_t row_bytes = (uint32_t)m.row_bytes;
   const uint32_t scale_ld = (uint32_t)m.scale_ld;
   u32x4 hreg[NQ][OPC];
+  float hsum[NQ];                                        // q4_0: sum of each held chunk of h_j
   int cur_j = -1;
   for (int i0 = sg * ips; i0 < i_end;) {
     const int j = i0 >> lrb;
@@ -338,6 +390,15 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int lrb) {
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
           for (int o = 0; o < OPC; ++o) hreg[q][o] = hp[(q * G + lg) * OPC + o];
+        if (FMT == OES_Q4_0) {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            float acc = 0.f;
+#pragma unroll
+            for (int o = 0; o < OPC; ++o) acc = sum8_bf16(hreg[q][o], acc);
+            hsum[q] = acc;
+          }
+        }
         cur_j = j;
       }
       // per-batch bases; per-row offsets stay 32-bit
@@ -360,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int lrb) {
             w[b][q] = __builtin_nontemporal_load(p + c);
             if (FMT == OES_FP8_BLOCK128)
               sc[b][q] = reinterpret_cast<const uint32_t *>(sb)[(uint32_t)(row >> 7) * scale_ld + (c >> 3)];
-            else if (FMT == OES_NVFP4)
+            else if (FMT == OES_NVFP4 || FMT == OES_Q4_0)
               sc[b][q] = reinterpret_cast<const uint16_t *>(sb + (uint32_t)row * scale_ld)[c];
             else
               sc[b][q] = 0;
@@ -372,7 +433,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int lrb) {
       for (int b = 0; b < IB; ++b) {
         if (b < cnt && row0 + b < a.H) {
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) acc[b] += dot_chunk<FMT>(w[b][q], sc[b][q], hreg[q]);
+          for (int q = 0; q < NQ; ++q)
+            acc[b] += dot_chunk<FMT>(w[b][q], sc[b][q], hreg[q], FMT == OES_Q4_0 ? hsum[q] : 0.f);
           acc[b] *= gl[b];  // the row's global multiplies every lane's partial sum
         }
       }
@@ -416,16 +478,23 @@ int pick_group_dn(int C, int k) {
   return 0;
 }
 
-// gate_up subgroups: the smallest G whose share is at most kMaxQ chunks per lane,
-// so each lane keeps up to 2 x kMaxQ 16-byte loads (gate and up rows) in flight.
-int pick_group_gu(int C) {
-  for (int g = 8; g <= 64; g *= 2)
-    if (C % g == 0 && C / g <= kMaxQ) return g;
-  return pick_group(C);
+// gate_up subgroups: the smallest G whose share is at most kMaxQ chunks per lane
+// (each lane keeps up to 2 x kMaxQ 16-byte loads, gate and up rows, in flight)
+// and whose grid still has 512 blocks (two per CU); short rows (few chunks) take
+// a wider G instead, trading loads in flight per lane for blocks.
+int pick_group_gu(int C, int I, int pairs) {
+  int last = 0;
+  for (int g = 8; g <= 64; g *= 2) {
+    if (C % g || C / g > kMaxQ) continue;
+    last = g;
+    const int64_t blocks = (int64_t)((I + kThreads / g - 1) / (kThreads / g)) * pairs;
+    if (blocks >= 512) return g;
+  }
+  return last ? last : pick_group(C);
 }
 
 int epc_of(int fmt) {
-  return fmt == OES_BF16 ? 8 : fmt == OES_FP8_BLOCK128 ? 16 : fmt == OES_NVFP4 ? 32 : 0;
+  return fmt == OES_BF16 ? 8 : fmt == OES_FP8_BLOCK128 ? 16 : (fmt == OES_NVFP4 || fmt == OES_Q4_0) ? 32 : 0;
 }
 
 Mat make_mat(const FfnArgs &a, bool down) {
@@ -439,7 +508,7 @@ Mat make_mat(const FfnArgs &a, bool down) {
   int bc = 0, bs = -1, bg = -1;
   if (fmt == OES_BF16) {
     bc = down ? 1 : 0;
-  } else if (fmt == OES_FP8_BLOCK128) {
+  } else if (fmt == OES_FP8_BLOCK128 || fmt == OES_Q4_0) {
     bc = down ? 2 : 0;
     bs = bc + 1;
   } else {
@@ -453,7 +522,7 @@ Mat make_mat(const FfnArgs &a, bool down) {
   if (bs >= 0) {
     m.scale = a.bank[bs];
     m.scale_slot = a.row_bytes[bs];
-    m.scale_ld = fmt == OES_FP8_BLOCK128 ? K / 128 : K / 16;
+    m.scale_ld = fmt == OES_FP8_BLOCK128 ? K / 128 : K / 16;  // nvfp4 / q4_0: bytes per row
   }
   if (bg >= 0) {
     m.glob = a.bank[bg];
@@ -467,24 +536,28 @@ hipError_t launch_gate_up_g(const KArgs &ka, hipStream_t s) {
   const FfnArgs &a = ka.f;
   constexpr int NSG = kThreads / G;
   dim3 grid((a.I + NSG - 1) / NSG, a.n * a.k);
-  hipLaunchKernelGGL((gate_up_kernel<FMT, G>), grid, dim3(kThreads), (size_t)a.H * 2, s, ka);
+  const size_t lds = (size_t)a.H * 2 + (FMT == OES_Q4_0 ? (size_t)(a.H / 32) * 4 : 0);
+  hipLaunchKernelGGL((gate_up_kernel<FMT, G>), grid, dim3(kThreads), lds, s, ka);
   return hipGetLastError();
 }
 
-// Rows per block: enough that every subgroup gets one full batch of IB rows of
-// one pair (RB * k = subgroups * IB), a power of two in [1, 16].
-int down_rows_per_block(int G, int NQ, int k) {
-  const int ib0 = NQ >= 2 ? 4 : 8;
-  const int ib = ib0 < G ? ib0 : G;
-  int rb = std::max(1, std::min(16, ib * (kThreads / G) / k));
-  while (rb & (rb - 1)) rb &= rb - 1;
+// Rows per block, a power of two in [1, 16]: the largest whose grid keeps about
+// three blocks per CU (768).  Every block reads each of its pairs' h rows once
+// per subgroup that takes that pair, so larger blocks cut that re-read; where
+// several subgroups share a pair (narrow G, small k) the re-read weighs more and
+// two blocks per CU (512) is the target.  Both targets were picked by timing
+// every (G, rows) choice on the decode workloads' shapes at 1, 2 and 8 tokens.
+int down_rows_per_block(int G, int k, int H, int n) {
+  const int64_t target = kThreads / G > k ? 512 : 768;
+  int rb = 16;
+  while (rb > 1 && (int64_t)((H + rb - 1) / rb) * n < target) rb >>= 1;
   return rb;
 }
 
 template <int FMT, int G, int NQ>
 hipError_t launch_down_gq(const KArgs &ka, hipStream_t s) {
   const FfnArgs &a = ka.f;
-  const int rb = down_rows_per_block(G, NQ, a.k);
+  const int rb = down_rows_per_block(G, a.k, a.H, a.n);
   int lrb = 0;
   while ((1 << lrb) < rb) ++lrb;
   dim3 grid((a.H + rb - 1) / rb, a.n);
@@ -506,7 +579,7 @@ hipError_t launch_down_g(const KArgs &ka, hipStream_t s) {
 template <int FMT>
 hipError_t launch_fmt(const KArgs &ka, hipStream_t s) {
   hipError_t e;
-  switch (pick_group_gu(ka.gu.C)) {
+  switch (pick_group_gu(ka.gu.C, ka.f.I, ka.f.n * ka.f.k)) {
     case 64: e = launch_gate_up_g<FMT, 64>(ka, s); break;
     case 32: e = launch_gate_up_g<FMT, 32>(ka, s); break;
     case 16: e = launch_gate_up_g<FMT, 16>(ka, s); break;
@@ -536,6 +609,16 @@ __global__ void debug_decode_kernel(int elem, const uint8_t *codes, int n, float
     return;
   }
   if (i >= n) return;
+  if (elem == OES_ELEM_Q4X2) {
+    // element i: block i / 32, position j; code byte j % 16 of the block, low
+    // nibble for j < 16; decoded by the FFN's permutation, minus the 128 + 8 offset
+    const int j = i % 32, bj = j % 16;
+    const uint32_t dw = reinterpret_cast<const uint32_t *>(codes + (i / 32) * 16)[bj / 4];
+    const uint32_t nib = j < 16 ? dw & 0x0f0f0f0fu : (dw >> 4) & 0x0f0f0f0fu;
+    const uint32_t pr = (bj % 4) < 2 ? q4_pair_bf16<0>(nib) : q4_pair_bf16<1>(nib);
+    out[i] = bf16_to_f32(bj % 2 ? pr >> 16 : pr & 0xffffu) - 136.f;
+    return;
+  }
   if (elem == OES_ELEM_E4M3) {
     out[i] = fp8_pair_f32<false>((uint32_t)codes[i]).x;
   } else if (elem == OES_ELEM_E8M0) {
@@ -554,7 +637,7 @@ bool expert_ffn_supported(int format, int H, int I, int k) {
   const int epc = epc_of(format);
   if (!epc) return false;
   if (H % epc || I % epc) return false;
-  const int gu = pick_group_gu(H / epc), dn = pick_group_dn(I / epc, k);
+  const int gu = pick_group_gu(H / epc, I, k), dn = pick_group_dn(I / epc, k);
   if (!gu || !dn) return false;  // down: at most 4 chunks per lane held in registers
   if (H > 16384) return false;          // x row staged in LDS by gate_up
   if (k > 32 || 16 * k > kMaxRed) return false;
@@ -570,6 +653,7 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t s) {
     case OES_BF16: return launch_fmt<OES_BF16>(ka, s);
     case OES_FP8_BLOCK128: return launch_fmt<OES_FP8_BLOCK128>(ka, s);
     case OES_NVFP4: return launch_fmt<OES_NVFP4>(ka, s);
+    case OES_Q4_0: return launch_fmt<OES_Q4_0>(ka, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,6 +21,8 @@ Encoders (public format recipes, not from the pages):
               q = e2m1(clip(w / (sc g), +-6)); two codes per byte, low nibble first
   mxfp4 (T)   per 32 along K, exponent e = clip(floor(log2 amax) - 2 + 127, 0, 254),
               q = e2m1(clip(w / 2**(e - 127), +-6)); blocks laid out [K/32, N, 16]
+  q4_0        per 32 along K d = fp16(max(amax, tiny) / 7), q = clip(round(w / d) + 8, 0, 15);
+              byte j of a block holds q_j | q_(j+16) << 4 (GGUF block_q4_0 order)
 e2m1 rounding is to nearest, ties to the even code.
 """
 import hashlib
@@ -28,7 +30,7 @@ import hashlib
 import numpy as np
 import torch
 
-FORMATS = ("bf16", "fp8_block128", "nvfp4", "mxfp4_t")
+FORMATS = ("bf16", "fp8_block128", "nvfp4", "mxfp4_t", "q4_0")
 WEIGHT_STD = 0.02
 
 

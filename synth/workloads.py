@@ -1,4 +1,4 @@
-"""The five synthetic workloads and builders for their host banks.
+"""The six synthetic workloads and builders for their host banks.
 
 Sizes follow the workloads the benchmark is quoted on; inputs are seeded
 (seed 0) and synthetic.  Only layer 0's host banks are filled, as the copy
@@ -42,6 +42,8 @@ WORKLOADS = {
                  miss_rates=(0.1, 0.5), note="fp8 128x128-block banks, 60 layers, 2048 slots"),
         Workload("nvfp4_h7168", "nvfp4", L=60, E=256, k=8, H=7168, I=2048, S=1536, batches=(1, 4),
                  miss_rates=(0.05, 0.25, 1.0), note="nvfp4 six-bank layout, 60 layers, 1536 slots"),
+        Workload("q4_0_h2048", "q4_0", L=48, E=128, k=8, H=2048, I=768, S=1024, batches=(1, 8),
+                 miss_rates=(0.25, 0.5), note="GGUF Q4_0 banks at the bf16 sweep's model shape, 1024 slots"),
         Workload("mxfp4_prefill", "mxfp4_t", L=4, E=128, k=4, H=2880, I=2880, S=0, tokens=2048,
                  stream_layers=4, note="mxfp4 transposed banks streamed per layer, 2048 tokens"),
     ]

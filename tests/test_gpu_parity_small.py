@@ -34,6 +34,8 @@ def _case(msg):
     (oes.ELEM_FP4X2, 256, lambda b: odecode.e2m1(odecode.fp4x2_unpack(b[None, :])[0])),
     (oes.ELEM_BF16, 65536 * 2, lambda b: odecode.bf16(b.view(np.uint16))),
     (oes.ELEM_FP16, 65536 * 2, lambda b: odecode.fp16(b.view(np.uint16))),
+    # 256 code bytes = 16 GGUF Q4_0 blocks, every byte value once
+    (oes.ELEM_Q4X2, 256, lambda b: odecode.q4_0(odecode.q4x2_unpack(b[None, :])[0])),
 ])
 def test_device_decoders_match_oracle(elem, nbytes, ref):
     _case(f"decode elem={elem}")
@@ -217,7 +219,7 @@ def test_lru_capacity_and_bad_ids_leave_state():
 # ------------------------------------------------------------------ copy
 @pytest.mark.parametrize("fmt,H,I,E,S,L", [
     ("bf16", 256, 128, 16, 8, 1), ("fp8_block128", 256, 256, 12, 5, 2), ("nvfp4", 512, 256, 10, 6, 1),
-    ("mxfp4_t", 64, 96, 9, 4, 2)])
+    ("mxfp4_t", 64, 96, 9, 4, 2), ("q4_0", 256, 512, 9, 5, 2)])
 @pytest.mark.parametrize("fused", [1, 0])
 def test_copy_missing_bytes(fmt, H, I, E, S, L, fused):
     _case(f"copy fmt={fmt} fused={fused}")
@@ -332,6 +334,13 @@ FFN_CASES += [
     ("bf16", 1536, 256, 12, 8, 5), ("bf16", 2048, 768, 8, 8, 5), ("fp8_block128", 4096, 512, 8, 6, 3),
     ("nvfp4", 7168, 1024, 8, 5, 2), ("bf16", 2048, 512, 8, 8, 3), ("bf16", 2048, 1024, 9, 8, 4),
 ]
+# GGUF Q4_0 (one 32-element block per 16-byte chunk): 8- to 64-lane subgroups,
+# 1 to 4 down chunks per lane, a skipped pair and a repeated routing
+FFN_CASES += [
+    ("q4_0", 256, 256, 8, 2, 3), ("q4_0", 512, 256, 7, 4, 2), ("q4_0", 2048, 768, 8, 8, 5),
+    ("q4_0", 7168, 1024, 8, 5, 2), ("q4_0", 4096, 2048, 6, 4, 3), ("q4_0", 1024, 4096, 5, 2, 1),
+    ("q4_0", 256, 8192, 4, 2, 1),
+]
 
 
 @pytest.mark.parametrize("fmt,H,I,E,k,n", FFN_CASES)
@@ -364,7 +373,7 @@ def test_expert_ffn_matches_oracle(fmt, H, I, E, k, n):
     ref = offn.expert_ffn(fmt, H, I, G.bits16(x), slot_ids, w.astype(np.float64),
                           lambda s: [host[b][0][perm[s]] for b in range(len(host))])
     got = G.bf16_tensor_to_f64(y)
-    tol = 3e-2 if fmt == "nvfp4" else 1e-2
+    tol = 3e-2 if fmt in ("nvfp4", "q4_0") else 1e-2
     err = offn.rel_l2(got, ref)
     print(f"  rel_l2={err:.3e}")
     assert err <= tol
