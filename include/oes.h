@@ -80,7 +80,8 @@ int32_t oes_abi_version(void);
  *                     bytes, byte j holds element j in its low nibble and
  *                     element j+16 in its high nibble), gate_up_d [2I,H/32] fp16,
  *                     down_q [H,I/2], down_d [H,I/32] (W = (q - 8) * d of its
- *                     32-block; the fifth format of architecture walk-through §5)
+ *                     32-block; the fifth format of FreeToken architecture walk-through §5,
+ *                     GGUF Q4_0 MoE in §6)
  */
 enum { OES_BF16 = 0, OES_FP8_BLOCK128 = 1, OES_NVFP4 = 2, OES_MXFP4_T = 3, OES_Q4_0 = 4 };
 enum {
