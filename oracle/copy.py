@@ -29,3 +29,18 @@ def copy_missing(misses, host_banks, slot_banks, num_experts: int):
             slot_banks[b][slot, :] = row
             moved += row.size
     return moved
+
+
+def resize_slots(slot_banks, src, fill: int = 0xA5):
+    """Slot banks after a pool resize (see SlotTable.resize): new slot i takes the
+    bytes of old slot src[i]; a new empty slot (src[i] = -1) holds `fill` here,
+    standing for bytes that no step reads before a copy writes them.
+    Returns new arrays; the inputs are not changed."""
+    out = []
+    for bank in slot_banks:
+        new = np.full((len(src), bank.shape[1]), fill, dtype=np.uint8)
+        for i, s in enumerate(src):
+            if s >= 0:
+                new[i, :] = bank[s]
+        out.append(new)
+    return out

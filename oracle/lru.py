@@ -74,6 +74,39 @@ class SlotTable:
     def snapshot(self):
         return self.owner.copy(), self.stamp.copy(), self.clock
 
+    def resize(self, num_slots: int) -> list:
+        """Runtime resize of the slot pool (FreeToken architecture walk-through §4:
+        VRAM moves between the expert cache and the KV cache at run time, with no
+        restart and no weight reload).
+
+        Readings (the page names the feature only): growing keeps every slot
+        where it is and appends empty slots; shrinking keeps the num_slots slots
+        that come last in the victim order of ensure() - empty slots leave
+        first, then the least recently used - and packs them, in ascending old
+        index, into slots [0, num_slots).  Stamps and the clock are kept, so the
+        kept experts keep their LRU order; the experts of the dropped slots are
+        no longer resident.
+
+        Returns src: new slot i holds what old slot src[i] held (-1: a new,
+        empty slot)."""
+        num_slots = int(num_slots)
+        if num_slots < 1:
+            raise ValueError("num_slots must be positive")
+        if num_slots >= self.S:
+            src = list(range(self.S)) + [-1] * (num_slots - self.S)
+        else:
+            order = sorted(range(self.S), key=lambda s: (int(self.owner[s]) != -1, int(self.stamp[s]),
+                                                         int(self.owner[s]), s))
+            src = sorted(order[self.S - num_slots:])
+        owner = np.full(num_slots, -1, dtype=np.int64)
+        stamp = np.zeros(num_slots, dtype=np.uint64)
+        for i, s in enumerate(src):
+            if s >= 0:
+                owner[i] = self.owner[s]
+                stamp[i] = self.stamp[s]
+        self.owner, self.stamp, self.S = owner, stamp, num_slots
+        return src
+
     def ensure(self, layer: int, ids) -> EnsureResult:
         ids = np.asarray(ids, dtype=np.int64)
         if ids.ndim == 1:

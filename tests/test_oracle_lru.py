@@ -11,6 +11,12 @@
    lru_hybrid_trace_s3_e4.txt); on random traces it equals the plain LRU step on
    the requests that keep a slot (overflow pairs map to -1); with a cap at or
    above the misses it equals the plain step; the cap's closed forms.
+5. Slot-pool resize: a hand-worked example (tests/golden/lru_resize_s5.txt);
+   the LRU stack property - a table shrunk to S' holds exactly what an
+   independent textbook LRU of S' slots holds after the same trace, and both
+   miss the same ids afterwards; a grown table behaves step for step like a
+   textbook LRU of the larger size given the same contents; the slot bytes
+   follow the slot map.
 """
 import itertools
 import os
@@ -297,3 +303,143 @@ def test_hybrid_without_cap_equals_plain():
         assert rp.status == OK and r.status == OK and r.overflow == []
         assert r.slot_ids.tolist() == rp.slot_ids.tolist() and r.misses == rp.misses
         assert r.num_indices == r.num_missing_full == len(rp.misses)
+
+
+# ------------------------------------------------------------------ resize
+def _golden_resize():
+    lines = [l.split("#")[0].split() for l in open(os.path.join(GOLDEN, "lru_resize_s5.txt"))]
+    return [l for l in lines if l]
+
+
+def _fields(tokens):
+    out, key = {}, None
+    for tok in tokens:
+        if tok.lstrip("-").isdigit() or ":" in tok:
+            out[key].append(tok)
+        else:
+            key = tok
+            out[key] = []
+    return out
+
+
+def test_resize_hand_worked():
+    lines = _golden_resize()
+    owner = [int(v) for v in lines[0][1:]]
+    stamp = [int(v) for v in lines[1][1:]]
+    clock = int(lines[2][1])
+    for line in lines[3:]:
+        t = SlotTable(len(owner), 1, 10)
+        t.set_state(owner, stamp, clock)
+        f = _fields(line)
+        if line[0] == "resize":
+            src = t.resize(int(f["resize"][0]))
+            assert src == [int(v) for v in f["src"]]
+            assert t.owner.tolist() == [int(v) for v in f["owner"]]
+            assert t.stamp.tolist() == [int(v) for v in f["stamp"]]
+            assert t.clock == clock and t.S == len(src)
+        else:  # a step after the shrink to 3
+            t.resize(3)
+            r = t.ensure(0, [[int(v) for v in f["ids"]]])
+            assert r.status == OK
+            assert r.slot_ids.tolist() == [[int(v) for v in f["slots"]]]
+            assert r.misses == [tuple(int(x) for x in m.split(":")) for m in f["misses"]]
+            assert t.owner.tolist() == [int(v) for v in f["owner"]]
+            assert t.stamp.tolist() == [int(v) for v in f["stamp"]]
+            assert t.clock == int(f["clock"][0])
+
+
+def _trace(rng, L, E, steps, max_distinct):
+    out = []
+    for _ in range(steps):
+        layer = rng.randrange(L)
+        n, k = rng.randint(1, 2), rng.randint(1, 2)
+        while True:
+            ids = [[rng.randrange(E) for _ in range(k)] for _ in range(n)]
+            if len({e for r in ids for e in r}) <= max_distinct:
+                break
+        out.append((layer, ids))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shrink_holds_what_a_smaller_lru_holds(seed):
+    """LRU is a stack algorithm: after any trace, a pool of S' slots holds the S'
+    most recently used ids, whatever larger pool ran beside it."""
+    rng = random.Random(100 + seed)
+    for _ in range(40):
+        L, E = rng.randint(1, 3), rng.randint(2, 7)
+        S = rng.randint(2, 8)
+        S2 = rng.randint(1, S)
+        before = _trace(rng, L, E, rng.randint(0, 30), min(S2, 4))
+        after = _trace(rng, L, E, 20, min(S2, 4))
+        big, small = SlotTable(S, L, E), TextbookLRU(S2, L, E)
+        for layer, ids in before:
+            assert big.ensure(layer, ids).status == OK
+            assert small.step(layer, ids) is not None
+        src = big.resize(S2)
+        assert sorted(o for o in big.owner.tolist() if o >= 0) == sorted(o for o in small.owner if o >= 0)
+        assert len(src) == S2 and sorted(s for s in src if s >= 0) == [s for s in src if s >= 0]
+        for layer, ids in after:
+            ra = big.ensure(layer, ids)
+            rb = small.step(layer, ids)
+            assert ra.status == OK and rb is not None
+            assert sorted(m[1] for m in ra.misses) == sorted(m[1] for m in rb[1])
+            assert sorted(o for o in big.owner.tolist() if o >= 0) == sorted(o for o in small.owner if o >= 0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_grow_behaves_like_a_larger_lru(seed):
+    rng = random.Random(200 + seed)
+    for _ in range(40):
+        L, E = rng.randint(1, 3), rng.randint(2, 8)
+        S = rng.randint(1, 5)
+        S2 = S + rng.randint(0, 4)
+        t = SlotTable(S, L, E)
+        for layer, ids in _trace(rng, L, E, rng.randint(0, 20), min(S, 4)):
+            assert t.ensure(layer, ids).status == OK
+        owner_before, stamp_before = t.owner.copy(), t.stamp.copy()
+        src = t.resize(S2)
+        assert src == list(range(S)) + [-1] * (S2 - S)
+        assert t.owner[:S].tolist() == owner_before.tolist() and (t.owner[S:] == -1).all()
+        assert t.stamp[:S].tolist() == stamp_before.tolist()
+        # the textbook LRU's recency list: empty slots by index, then by (stamp, owner)
+        empty = [s for s in range(S2) if t.owner[s] == -1]
+        used = sorted((s for s in range(S2) if t.owner[s] >= 0), key=lambda s: (int(t.stamp[s]), int(t.owner[s])))
+        ref = TextbookLRU(S2, L, E, owner=t.owner.tolist(), order=empty + used)
+        for layer, ids in _trace(rng, L, E, 20, min(S2, 5)):
+            ra, rb = t.ensure(layer, ids), ref.step(layer, ids)
+            if rb is None:
+                assert ra.status == ERR_CAPACITY
+                continue
+            assert ra.status == OK
+            assert ra.slot_ids.tolist() == rb[0] and ra.misses == rb[1]
+
+
+def test_resize_same_size_and_round_trip():
+    rng = np.random.default_rng(3)
+    t = SlotTable(6, 2, 5)
+    for _ in range(12):
+        t.ensure(int(rng.integers(2)), rng.integers(0, 5, size=(1, 2)))
+    o, st, c = t.snapshot()
+    assert t.resize(6) == list(range(6))
+    assert t.owner.tolist() == o.tolist() and t.stamp.tolist() == st.tolist() and t.clock == c
+    kept = t.resize(3)
+    survivors = {int(o[s]) for s in kept if o[s] >= 0}
+    t.resize(9)
+    assert {int(v) for v in t.owner.tolist() if v >= 0} == survivors
+    with pytest.raises(ValueError):
+        t.resize(0)
+
+
+def test_resize_moves_slot_bytes():
+    rng = np.random.default_rng(5)
+    banks = [rng.integers(0, 256, size=(5, rb), dtype=np.uint8) for rb in (32, 16)]
+    t = SlotTable(5, 1, 10)
+    t.set_state([7, -1, 3, 9, 4], [2, 0, 5, 5, 1], 5)
+    src = t.resize(3)
+    new = ocopy.resize_slots(banks, src)
+    for b in range(2):
+        assert np.array_equal(new[b], banks[b][[0, 2, 3]])
+    grown = ocopy.resize_slots(banks, list(range(5)) + [-1])
+    for b in range(2):
+        assert np.array_equal(grown[b][:5], banks[b]) and (grown[b][5] == 0xA5).all()
