@@ -21,7 +21,8 @@ Also printed (same JSON line): the copy sweep of the benchmark guide's columns
 miss rate, the measured ceilings (pinned H2D by DMA and by the zero-copy
 kernel, HBM streaming read, bf16 MFMA loop), the roofline of the dominant kernel and of the
 FFN, the cold decode FFN of every decode bank format (bf16, fp8 block, nvfp4,
-GGUF Q4_0) at its workload's shape, the MXFP4 prefill layer (grouped FFN on MFMA, whole-layer stream, the
+GGUF Q4_0) at its workload's shape, a slot-pool resize (half the slots and back),
+the MXFP4 prefill layer (grouped FFN on MFMA, whole-layer stream, the
 overlapped loop over 4 layers) and the CPU oracle timed on this host.
 """
 import argparse
@@ -268,6 +269,9 @@ def main():
         cache.set_option(oes.OPT_FUSED_COPY, 1)
         cache.check()
 
+    # ---------------------------------------------------------------- slot-pool resize
+    resize = _resize(cache, w, bpe, log)
+
     # ---------------------------------------------------------------- rooflines
     head, total, parts = headline
     ffn_gbs = ffn_bytes / (ffn_alone_ms * 1e6)
@@ -319,10 +323,32 @@ def main():
                    "misses": head["misses"], "active": active, "bytes_per_expert": bpe},
         "tok_ms": head["tok_ms"], "copy_GBps": head.get("copy_GBps"),
         "roofline": roof, "kernels": kernels, "probes": probes, "decode_per_miss_rate": per_mr,
-        "copy_sweep": sweep, "ffn_formats": ffn_formats, "prefill": prefill, "cpu_baseline": cpu,
+        "copy_sweep": sweep, "ffn_formats": ffn_formats, "resize": resize, "prefill": prefill, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     cache.close()
+
+
+def _resize(cache, w, bpe, log):
+    """Slot-pool resize on the bench cache (host-synchronous calls, wall clock):
+    shrink to half the slots, then grow back.  Each call moves half the slots'
+    rows (every kept slot, bpe bytes each) device to device, besides allocating
+    the new banks and table and freeing the old ones."""
+    import torch
+
+    torch.cuda.synchronize()
+    half = w.S // 2
+    t0 = time.perf_counter()
+    cache.resize(half)
+    t1 = time.perf_counter()
+    cache.resize(w.S)
+    t2 = time.perf_counter()
+    moved = half * bpe
+    out = {"slots": w.S, "shrunk_to": half, "moved_bytes": moved, "shrink_ms": (t1 - t0) * 1e3,
+           "grow_ms": (t2 - t1) * 1e3, "shrink_GBps": moved / ((t1 - t0) * 1e9),
+           "grow_GBps": moved / ((t2 - t1) * 1e9)}
+    log("resize", {k: (round(v, 3) if isinstance(v, float) else v) for k, v in out.items()})
+    return out
 
 
 def _ffn_formats(workloads, nsets, launches, probes, log):

@@ -168,6 +168,29 @@ oes_status oes_cache_set_state(oes_cache *c, const int64_t *owner, const uint64_
 oes_status oes_cache_snapshot(oes_cache *c, void *stream);
 oes_status oes_cache_restore(oes_cache *c, void *stream);
 
+/* Resize the slot pool to num_slots slots at run time, keeping the resident
+ * experts' bytes (no reload from the host banks) and their LRU order
+ * (FreeToken architecture walk-through §4: VRAM moves between the expert cache
+ * and other uses with no restart and no weight reload).
+ *   grow:   every slot keeps its index, contents, owner and stamp; the new
+ *           slots are empty (their bytes are undefined until a copy fills them).
+ *   shrink: the kept slots are the num_slots that come last in the remap's
+ *           victim order (empty slots leave first, then the least recently
+ *           used: key (not empty, stamp, owner, slot)); they move, in
+ *           ascending old index, to slots [0, num_slots).  The experts of the
+ *           other slots are no longer resident.
+ * Stamps, clock and the counters of oes_cache_stats are kept; the miss list of
+ * the last step and the load list are cleared (copy_missing then moves
+ * nothing), and a snapshot is discarded (restore returns OES_ERR_STATE).  A
+ * resize to the current size changes nothing.
+ * slot_ids of earlier steps name old slots: remap before the next FFN.
+ * Synchronous: syncs `stream` first (every enqueued step finishes), moves the
+ * rows with a device kernel, syncs again.  New banks and table are allocated
+ * before the old ones are freed, so the device briefly holds both; on any
+ * error the cache is unchanged.  Errors: OES_ERR_ARG (num_slots outside
+ * [1, OES_MAX_SLOTS]), OES_ERR_NOMEM, OES_ERR_HIP. */
+oes_status oes_cache_resize(oes_cache *c, int32_t num_slots, void *stream);
+
 /* Read the slot table into host arrays of num_slots entries (any pointer may
  * be NULL).  Syncs `stream`. */
 oes_status oes_cache_get_state(oes_cache *c, int64_t *owner, uint64_t *stamp, uint64_t *clock,

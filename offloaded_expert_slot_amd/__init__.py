@@ -10,7 +10,7 @@ The names follow the C ABI in ``include/oes.h``:
 
     schema_make(format, L, E, H, I)            -> Schema
     Cache(schema, num_slots, device)           .set_source / .set_state / .get_state
-                                               .ensure_experts / .copy_missing / .expert_ffn
+                                               .ensure_experts / .copy_missing / .expert_ffn / .resize
     route(x, wg, k, ...) / route_logits(logits, k, ...)
     Layers(schema, depth, device)              .set_source / .prefetch / .ffn
 """
@@ -31,6 +31,7 @@ OPT_FUSED_COPY, OPT_COPY_MODE, OPT_COPY_BLOCKS = 1, 2, 3
 COPY_ZERO, COPY_SDMA = 0, 1
 OK, ERR_ARG, ERR_CAPACITY, ERR_HIP, ERR_NOMEM, ERR_STATE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 MAX_BANKS = 6
+MAX_SLOTS = 4096
 
 
 class OesError(RuntimeError):
@@ -114,6 +115,7 @@ _SIGS = {
     "oes_probe_hbm_read": (_I32, [_P, _I64, _I64, _I32, _P, _P, _PF]),
     "oes_probe_mfma_bf16": (_I32, [_I32, _I32, _P, _P, _PF, ctypes.POINTER(ctypes.c_double)]),
     "oes_debug_decode": (_I32, [_I32, _P, _I32, _P, _P]),
+    "oes_cache_resize": (_I32, [_P, _I32, _P]),
 }
 
 
@@ -233,6 +235,11 @@ class Cache:
         _check(lib().oes_cache_get_state(self._h, owner.ctypes.data_as(_PI64), stamp.ctypes.data_as(_PU64),
                                          ctypes.byref(clock), _stream(stream)))
         return owner, stamp, int(clock.value)
+
+    def resize(self, num_slots, stream=None):
+        """Grow or shrink the slot pool in place (resident experts and their LRU order kept)."""
+        _check(lib().oes_cache_resize(self._h, int(num_slots), _stream(stream)))
+        self.num_slots = int(num_slots)
 
     def snapshot(self, stream=None):
         _check(lib().oes_cache_snapshot(self._h, _stream(stream)))

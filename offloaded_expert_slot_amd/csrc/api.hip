@@ -274,6 +274,80 @@ extern "C" oes_status oes_schema_make(int32_t format, int32_t L, int32_t E, int3
 }
 
 // ============================================================================ cache lifecycle
+// The slot table of S slots in one device block (owner | stamp | ctl | miss list |
+// load list) plus its pinned staging buffer.
+struct TableBufs {
+  uint8_t *dblock = nullptr;
+  int64_t *owner = nullptr;
+  uint64_t *stamp = nullptr;
+  Ctl *ctl = nullptr;
+  int32_t *miss_slot = nullptr;
+  int64_t *miss_id = nullptr;
+  int32_t *aux_slot = nullptr;
+  int64_t *aux_id = nullptr;
+  uint8_t *staging = nullptr;
+  int64_t staging_bytes = 0;
+};
+
+static void table_free(TableBufs *t) {
+  if (t->dblock) (void)hipFree(t->dblock);
+  if (t->staging) (void)hipHostFree(t->staging);
+  *t = TableBufs();
+}
+
+static oes_status table_alloc(int64_t S, TableBufs *t) {
+  *t = TableBufs();
+  int64_t off = 0;
+  const int64_t o_owner = off; off = round_up(off + 8 * S, 256);
+  const int64_t o_stamp = off; off = round_up(off + 8 * S, 256);
+  const int64_t o_ctl = off;   off = round_up(off + (int64_t)sizeof(Ctl), 256);
+  const int64_t o_ms = off;    off = round_up(off + 4 * S, 256);
+  const int64_t o_mi = off;    off = round_up(off + 8 * S, 256);
+  const int64_t o_as = off;    off = round_up(off + 4 * S, 256);
+  const int64_t o_ai = off;    off = round_up(off + 8 * S, 256);
+  hipError_t e = hipMalloc(&t->dblock, off);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    t->dblock = nullptr;
+    return fail(OES_ERR_NOMEM, "hipMalloc of the slot table failed");
+  }
+  t->owner = reinterpret_cast<int64_t *>(t->dblock + o_owner);
+  t->stamp = reinterpret_cast<uint64_t *>(t->dblock + o_stamp);
+  t->ctl = reinterpret_cast<Ctl *>(t->dblock + o_ctl);
+  t->miss_slot = reinterpret_cast<int32_t *>(t->dblock + o_ms);
+  t->miss_id = reinterpret_cast<int64_t *>(t->dblock + o_mi);
+  t->aux_slot = reinterpret_cast<int32_t *>(t->dblock + o_as);
+  t->aux_id = reinterpret_cast<int64_t *>(t->dblock + o_ai);
+  t->staging_bytes = round_up(16 * S + (int64_t)sizeof(Ctl) + 12 * S + 64, 256);
+  e = hipHostMalloc(reinterpret_cast<void **>(&t->staging), t->staging_bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    t->staging = nullptr;
+    table_free(t);
+    return fail(OES_ERR_NOMEM, "hipHostMalloc of the staging buffer failed");
+  }
+  return OES_OK;
+}
+
+static void table_adopt(oes_cache *c, const TableBufs &t) {
+  c->dblock = t.dblock;
+  c->owner = t.owner;
+  c->stamp = t.stamp;
+  c->ctl = t.ctl;
+  c->miss_slot = t.miss_slot;
+  c->miss_id = t.miss_id;
+  c->aux_slot = t.aux_slot;
+  c->aux_id = t.aux_id;
+  c->staging = t.staging;
+  c->staging_bytes = t.staging_bytes;
+}
+
+static int pad_pow2(int S) {
+  int p = 2;
+  while (p < S) p <<= 1;
+  return p;
+}
+
 static void cache_free(oes_cache *c) {
   for (int b = 0; b < OES_MAX_BANKS; ++b)
     if (c->slot_bank[b]) (void)hipFree(c->slot_bank[b]);
@@ -311,8 +385,7 @@ extern "C" oes_status oes_cache_create(const oes_schema *sc, int32_t num_slots, 
   c->S = num_slots;
   c->device = device;
   c->maxM = std::min(num_slots, sc->num_experts);
-  c->Spad = 2;
-  while (c->Spad < num_slots) c->Spad <<= 1;
+  c->Spad = pad_pow2(num_slots);
   for (int b = 0; b < sc->num_banks; ++b) {
     e = hipMalloc(&c->slot_bank[b], (size_t)num_slots * sc->bank[b].row_bytes);
     if (e != hipSuccess) {
@@ -323,33 +396,14 @@ extern "C" oes_status oes_cache_create(const oes_schema *sc, int32_t num_slots, 
     }
   }
   const int64_t S = num_slots;
-  int64_t off = 0;
-  const int64_t o_owner = off; off = round_up(off + 8 * S, 256);
-  const int64_t o_stamp = off; off = round_up(off + 8 * S, 256);
-  const int64_t o_ctl = off;   off = round_up(off + (int64_t)sizeof(Ctl), 256);
-  const int64_t o_ms = off;    off = round_up(off + 4 * S, 256);
-  const int64_t o_mi = off;    off = round_up(off + 8 * S, 256);
-  const int64_t o_as = off;    off = round_up(off + 4 * S, 256);
-  const int64_t o_ai = off;    off = round_up(off + 8 * S, 256);
-  e = hipMalloc(&c->dblock, off);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    cache_free(c);
-    return fail(OES_ERR_NOMEM, "hipMalloc of the slot table failed");
-  }
-  c->owner = reinterpret_cast<int64_t *>(c->dblock + o_owner);
-  c->stamp = reinterpret_cast<uint64_t *>(c->dblock + o_stamp);
-  c->ctl = reinterpret_cast<Ctl *>(c->dblock + o_ctl);
-  c->miss_slot = reinterpret_cast<int32_t *>(c->dblock + o_ms);
-  c->miss_id = reinterpret_cast<int64_t *>(c->dblock + o_mi);
-  c->aux_slot = reinterpret_cast<int32_t *>(c->dblock + o_as);
-  c->aux_id = reinterpret_cast<int64_t *>(c->dblock + o_ai);
-  c->staging_bytes = round_up(16 * S + (int64_t)sizeof(Ctl) + 12 * S + 64, 256);
-  e = hipHostMalloc(reinterpret_cast<void **>(&c->staging), c->staging_bytes, hipHostMallocDefault);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    cache_free(c);
-    return fail(OES_ERR_NOMEM, "hipHostMalloc of the staging buffer failed");
+  {
+    TableBufs t;
+    st = table_alloc(S, &t);
+    if (st != OES_OK) {
+      cache_free(c);
+      return st;
+    }
+    table_adopt(c, t);
   }
   e = hipEventCreateWithFlags(&c->staging_done, hipEventDisableTiming);
   if (e != hipSuccess) { cache_free(c); return hip_fail(e, "hipEventCreate"); }
@@ -542,6 +596,124 @@ extern "C" oes_status oes_cache_check(oes_cache *c, void *stream) {
   if (ctl.err == OES_ERR_ARG)
     return fail(OES_ERR_ARG, "a step held an expert id outside [0, %d) or a layer without a source", c->sc.num_experts);
   return fail(ctl.err, "device error %d", ctl.err);
+}
+
+// Runtime resize of the slot pool (FreeToken architecture walk-through §4: VRAM
+// moves between the expert cache and other uses with no restart and no weight
+// reload).  Growing keeps every slot in place and appends empty ones; shrinking
+// keeps the num_slots slots that come last in the remap's victim order (empty
+// slots first, then least recently used: key (not empty, stamp, owner, slot)),
+// packed in ascending old index.  Stamps, clock and counters are kept; the
+// pending miss and load lists are cleared.  New banks and table are allocated
+// and filled before the old ones are freed, so a failure leaves the cache as
+// it was.
+extern "C" oes_status oes_cache_resize(oes_cache *c, int32_t num_slots, void *stream) {
+  if (!c) return fail(OES_ERR_ARG, "cache is NULL");
+  if (num_slots < 1 || num_slots > OES_MAX_SLOTS)
+    return fail(OES_ERR_ARG, "num_slots %d outside [1, %d]", num_slots, OES_MAX_SLOTS);
+  DeviceGuard g(c->device);
+  if (!g.ok) return fail(OES_ERR_HIP, "hipSetDevice(%d) failed", c->device);
+  hipStream_t s = as_stream(stream);
+  const int S0 = c->S, S1 = num_slots;
+  // the current table; the sync also drains every step enqueued before
+  oes_status st = staging_acquire(c);
+  if (st != OES_OK) return st;
+  HIP_TRY(hipMemcpyAsync(c->staging, c->owner, 8 * (size_t)S0, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(c->staging + 8 * (size_t)S0, c->stamp, 8 * (size_t)S0, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(c->staging + 16 * (size_t)S0, c->ctl, sizeof(Ctl), hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  std::vector<int64_t> own0(S0);
+  std::vector<uint64_t> stp0(S0);
+  Ctl ctl;
+  memcpy(own0.data(), c->staging, 8 * (size_t)S0);
+  memcpy(stp0.data(), c->staging + 8 * (size_t)S0, 8 * (size_t)S0);
+  memcpy(&ctl, c->staging + 16 * (size_t)S0, sizeof(Ctl));
+  if (S1 == S0) return OES_OK;
+
+  // new slot i takes old slot src[i] (-1: new and empty)
+  std::vector<int32_t> src(S1, -1);
+  if (S1 > S0) {
+    for (int i = 0; i < S0; ++i) src[i] = i;
+  } else {
+    std::vector<int32_t> order(S0);
+    for (int i = 0; i < S0; ++i) order[i] = i;
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      const bool ea = own0[a] != -1, eb = own0[b] != -1;
+      if (ea != eb) return !ea;
+      if (stp0[a] != stp0[b]) return stp0[a] < stp0[b];
+      if (own0[a] != own0[b]) return own0[a] < own0[b];
+      return a < b;
+    });
+    std::vector<int32_t> keep(order.end() - S1, order.end());
+    std::sort(keep.begin(), keep.end());
+    src = keep;
+  }
+  std::vector<int64_t> own1(S1, -1);
+  std::vector<uint64_t> stp1(S1, 0);
+  for (int i = 0; i < S1; ++i)
+    if (src[i] >= 0) {
+      own1[i] = own0[src[i]];
+      stp1[i] = stp0[src[i]];
+    }
+
+  // new table and banks
+  TableBufs t;
+  st = table_alloc(S1, &t);
+  if (st != OES_OK) return st;
+  uint8_t *nb[OES_MAX_BANKS] = {};
+  auto drop_new = [&]() {
+    for (int b = 0; b < OES_MAX_BANKS; ++b)
+      if (nb[b]) (void)hipFree(nb[b]);
+    table_free(&t);
+  };
+  for (int b = 0; b < c->sc.num_banks; ++b) {
+    hipError_t e = hipMalloc(&nb[b], (size_t)S1 * c->sc.bank[b].row_bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      nb[b] = nullptr;
+      drop_new();
+      return fail(OES_ERR_NOMEM, "hipMalloc of slot bank %s (%lld bytes) failed", c->sc.bank[b].name,
+                  (long long)S1 * c->sc.bank[b].row_bytes);
+    }
+  }
+  Ctl nc = ctl;
+  nc.miss_count = 0;
+  nc.aux_count = 0;
+  uint8_t *p = t.staging;
+  memcpy(p, own1.data(), 8 * (size_t)S1);
+  memcpy(p + 8 * (size_t)S1, stp1.data(), 8 * (size_t)S1);
+  memcpy(p + 16 * (size_t)S1, &nc, sizeof(Ctl));
+  memcpy(p + 16 * (size_t)S1 + sizeof(Ctl), src.data(), 4 * (size_t)S1);
+  hipError_t e = hipMemcpyAsync(t.owner, p, 8 * (size_t)S1, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(t.stamp, p + 8 * (size_t)S1, 8 * (size_t)S1, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(t.ctl, p + 16 * (size_t)S1, sizeof(Ctl), hipMemcpyHostToDevice, s);
+  // the move list goes to the new load-list area, unused until the next load_rows
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(t.aux_slot, p + 16 * (size_t)S1 + sizeof(Ctl), 4 * (size_t)S1, hipMemcpyHostToDevice, s);
+  for (int b = 0; b < c->sc.num_banks && e == hipSuccess; ++b)
+    e = launch_slot_move(nb[b], c->slot_bank[b], t.aux_slot, S1, c->sc.bank[b].row_bytes, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipStreamSynchronize(s);  // nothing enqueued may still use the new buffers
+    drop_new();
+    return hip_fail(e, "moving the slot rows");
+  }
+
+  // swap in
+  for (int b = 0; b < OES_MAX_BANKS; ++b) {
+    if (c->slot_bank[b]) (void)hipFree(c->slot_bank[b]);
+    c->slot_bank[b] = nb[b];
+  }
+  (void)hipFree(c->dblock);
+  (void)hipHostFree(c->staging);
+  table_adopt(c, t);
+  if (c->snap) (void)hipFree(c->snap);
+  c->snap = nullptr;
+  c->has_snap = false;
+  c->S = S1;
+  c->maxM = std::min(S1, c->sc.num_experts);
+  c->Spad = pad_pow2(S1);
+  return OES_OK;
 }
 
 extern "C" oes_status oes_cache_stats(oes_cache *c, oes_stats *out, void *stream) {

@@ -113,7 +113,33 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4 *src, int64_t
   if (acc == 0x7f3a9e11u) sink[0] = (float)acc;
 }
 
+// Slot-pool resize: row i of the new bank takes row src[i] of the old bank
+// (src[i] = -1: a new empty slot, left as it is).  Rows are multiples of 16
+// bytes; blocks stride over rows (y) and 16-byte chunks of a row (x).
+__global__ __launch_bounds__(256) void slot_move_kernel(uint8_t *dst, const uint8_t *src_bank, const int32_t *src,
+                                                        int n, int64_t row_bytes) {
+  const int64_t n16 = row_bytes >> 4;
+  for (int i = blockIdx.y; i < n; i += gridDim.y) {
+    const int r = src[i];
+    if (r < 0) continue;
+    const u32x4 *a = reinterpret_cast<const u32x4 *>(src_bank + (int64_t)r * row_bytes);
+    u32x4 *b = reinterpret_cast<u32x4 *>(dst + (int64_t)i * row_bytes);
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n16; c += (int64_t)gridDim.x * blockDim.x)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(a + c), b + c);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_slot_move(uint8_t *dst, const uint8_t *src_bank, const int32_t *src, int n, int64_t row_bytes,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n16 = row_bytes >> 4;
+  const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(64, (n16 + 255) / 256));
+  const int gy = std::min(n, 1024);
+  hipLaunchKernelGGL(slot_move_kernel, dim3(gx, gy), dim3(256), 0, s, dst, src_bank, src, n, row_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const CopyArgs &a, int blocks, hipStream_t s) {
   hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, s, a);

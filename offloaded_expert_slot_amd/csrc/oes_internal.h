@@ -64,6 +64,9 @@ struct CopyArgs {
 constexpr int COPY_UNROLL = 8;                       // 16-byte loads in flight per lane
 constexpr int64_t COPY_CHUNK = 64 * 16 * COPY_UNROLL;  // bytes one wave moves per work item
 hipError_t launch_gather(const CopyArgs &a, int blocks, hipStream_t s);
+// new_bank row i <- old_bank row src[i] for i < n (src[i] = -1: skipped); src on the device
+hipError_t launch_slot_move(uint8_t *dst, const uint8_t *src_bank, const int32_t *src, int n, int64_t row_bytes,
+                            hipStream_t s);
 
 // ---------------------------------------------------------------- route
 int route_splits(int H, int E);

@@ -10,6 +10,8 @@ expert count, full slot pool with every slot owned by another layer):
 * the bs=1 decode step (route -> ensure -> copy -> FFN) must match the oracle:
   slot map and misses exactly, y to the relative-L2 bound of the format.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -210,3 +212,77 @@ def test_hybrid_step_bs8(max_fetch, frac):
     err = offn.rel_l2(G.bf16_tensor_to_f64(y), ref)
     print(f"  fetched {r.num_indices} of {r.num_missing_full} misses, rel_l2={err:.3e}")
     assert err <= 1e-2
+
+
+@pytest.mark.timeout(600)
+def test_resize_full_size():
+    """Slot-pool resize at the bench workload's size (1024 slots of 9 MiB): shrink to
+    300 and grow back; the table matches the oracle and every kept slot keeps its
+    bytes (the host row of its layer-0 owner, else the fill)."""
+    w, hb, _ = _setup("bf16_h2048")
+    _case("resize bf16_h2048 1024 -> 300 -> 1024")
+    dev = G.dev()
+    sc = oes.schema_make(w.fmt, w.L, w.E, w.H, w.I)
+    c = oes.Cache(sc, w.S, 0)
+    for b, t in enumerate(hb.banks):
+        c.set_source(b, 0, t)
+    c.fill_slots(0xA5)
+    rng = np.random.default_rng(31)
+    perm = rng.permutation(w.S)
+    owner = np.full(w.S, -1, dtype=np.int64)
+    local = perm[: w.E]                                # layer-0 experts, one per slot
+    owner[local] = rng.permutation(w.E)
+    foreign = perm[w.E: w.E + 500]                     # experts of other layers (no bytes)
+    owner[foreign] = w.E + rng.choice((w.L - 1) * w.E, size=500, replace=False)
+    stamp = np.where(owner >= 0, rng.integers(1, 400, size=w.S), 0).astype(np.uint64)  # ties on purpose
+    c.set_state(owner, stamp, 400)
+    c.load_rows(local.tolist(), owner[local].tolist())
+    t = SlotTable(w.S, w.L, w.E)
+    t.set_state(owner, stamp, 400)
+
+    def check_bytes(carried):
+        """Layer-0 owners hold their host rows; other carried-over slots the fill
+        (slots past `carried` are new after a grow: their bytes are undefined)."""
+        own = t.owner
+        loc = np.nonzero((own >= 0) & (own < w.E))[0]
+        rest = np.nonzero(~((own >= 0) & (own < w.E)))[0]
+        li = torch.from_numpy(loc).to(dev)
+        ei = torch.from_numpy(own[loc]).to(dev)
+        for b in range(sc.num_banks):
+            view = c.slot_bank_view(b)
+            rb = hb.row_bytes[b]
+            want = hb.banks[b].view(w.E, rb).to(dev)[ei]
+            assert torch.equal(view[li], want), b
+            kept_fill = [s for s in rest if s < carried]
+            if kept_fill:
+                assert bool((view[torch.tensor(kept_fill, device=dev)] == 0xA5).all()), b
+
+    t0 = time.perf_counter()
+    c.resize(300)
+    ms_shrink = (time.perf_counter() - t0) * 1e3
+    src = t.resize(300)
+    got_owner, got_stamp, clock = c.get_state()
+    assert got_owner.tolist() == t.owner.tolist() and got_stamp.tolist() == t.stamp.tolist() and clock == 400
+    assert sum(1 for s in src if owner[s] >= 0 and owner[s] < w.E) == int(((t.owner >= 0) & (t.owner < w.E)).sum())
+    check_bytes(300)
+    t0 = time.perf_counter()
+    c.resize(w.S)
+    ms_grow = (time.perf_counter() - t0) * 1e3
+    t.resize(w.S)
+    got_owner, got_stamp, _ = c.get_state()
+    assert got_owner.tolist() == t.owner.tolist() and got_stamp.tolist() == t.stamp.tolist()
+    check_bytes(300)
+    print(f"  shrink {ms_shrink:.1f} ms, grow {ms_grow:.1f} ms", flush=True)
+    # a step after the resizes: the remap and the copy agree with the oracle
+    ids = synth.synthetic_ids(8, w.k, w.E, 0, w.name).numpy()
+    d_ids = torch.from_numpy(ids).to(dev)
+    d_slots = torch.empty_like(d_ids)
+    c.ensure_experts(0, d_ids, d_slots)
+    c.copy_missing()
+    torch.cuda.synchronize()
+    c.check()
+    r = t.ensure(0, ids)
+    assert r.status == OK
+    assert np.array_equal(d_slots.cpu().numpy(), r.slot_ids)
+    assert c.get_misses() == r.misses
+    c.close()
