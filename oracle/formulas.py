@@ -59,3 +59,21 @@ def hybrid_fetch_fraction(pcie_gbps: float, cpu_gbps: float) -> float:
     if cpu_gbps <= pcie_gbps:
         return 1.0
     return pcie_gbps / cpu_gbps
+
+
+# Formats whose experts the CPU executor can compute (FreeToken MoE benchmark
+# guide §5.2: a format with no CPU MoE weight path - block fp8 is the page's
+# example - always stays offload).  Which formats have one is a reading: bf16,
+# NVFP4 and GGUF Q4_0 (the decode formats other than block fp8; the MXFP4 banks
+# here are the transposed prefill layout).
+CPU_FORMATS = ("bf16", "nvfp4", "q4_0")
+
+
+def recommend_backend(fmt: str, cpu_gbps: float, pcie_gbps: float, threshold: float = 2.0) -> str:
+    """ft bench bw's per-(workload, format) decision (benchmark guide §5.2):
+    "hybrid" when the CPU MoE kernel's bandwidth exceeds threshold (default 2)
+    times the PCIe gather bandwidth and the format has a CPU path, else
+    "offload".  Reading: "exceeds" is strict."""
+    if fmt not in CPU_FORMATS:
+        return "offload"
+    return "hybrid" if cpu_gbps > threshold * pcie_gbps else "offload"

@@ -63,3 +63,17 @@ def test_copy_mib_and_tok_ms():
     assert F.decode_tok_s(0.25, 48) == pytest.approx(1000.0 / 12.0)
     with pytest.raises(ValueError):
         F.bw_gbps(1, 1, 0.0)
+
+
+def test_recommend_backend_closed_forms():
+    """Benchmark guide §5.2: hybrid iff the CPU kernel beats threshold x the PCIe gather,
+    and only for formats with a CPU path."""
+    assert F.recommend_backend("bf16", 120.0, 56.0) == "hybrid"      # 120 > 2 * 56
+    assert F.recommend_backend("bf16", 112.0, 56.0) == "offload"     # equal: not exceeding
+    assert F.recommend_backend("bf16", 100.0, 56.0) == "offload"
+    assert F.recommend_backend("nvfp4", 100.0, 40.0, threshold=2.5) == "offload"
+    assert F.recommend_backend("nvfp4", 100.1, 40.0, threshold=2.5) == "hybrid"
+    assert F.recommend_backend("q4_0", 57.0, 56.0, threshold=1.0) == "hybrid"
+    assert F.recommend_backend("fp8_block128", 1e6, 1.0) == "offload"
+    assert F.recommend_backend("mxfp4_t", 1e6, 1.0) == "offload"
+    assert set(F.CPU_FORMATS) == {"bf16", "nvfp4", "q4_0"}
