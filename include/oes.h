@@ -373,6 +373,80 @@ oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *
                                double *flops);
 
 /* ------------------------------------------------------------------ decoder check */
+/* ---------------------------------------------------------------- hybrid backend
+ * CPU MoE executor (FreeToken architecture walk-through §5: what PCIe cannot
+ * bring in time is computed by the host cores with AVX-512 GEMVs; FreeToken
+ * MoE benchmark guide §5.2-§5.4: ensure_experts_hybrid hands the experts above
+ * the fetch cap (slot -1) to this executor).  Host code: every pointer below is
+ * a host pointer, nothing touches the GPU, calls block until done.  Formats
+ * with a CPU path: OES_BF16, OES_NVFP4, OES_Q4_0.  An executor is not
+ * thread-safe: use it from one thread. */
+typedef struct oes_cpu_moe oes_cpu_moe;
+
+/* Create an executor for `schema` with `threads` worker threads (0: one per
+ * CPU of the process's affinity mask; the calling thread is one of them).
+ * Errors: OES_ERR_ARG (schema not from oes_schema_make, threads outside
+ * [0, 1024]), OES_ERR_UNSUPPORTED (a format without a CPU path, or a host
+ * without AVX-512 F/BW/VL/BF16 and F16C). */
+oes_status oes_cpu_moe_create(const oes_schema *schema, int32_t threads, oes_cpu_moe **out);
+oes_status oes_cpu_moe_destroy(oes_cpu_moe *m);
+oes_status oes_cpu_moe_threads(const oes_cpu_moe *m, int32_t *threads);
+
+/* Register bank `bank` of layer `layer`: E rows of row_bytes, expert-major,
+ * the same host tensors a cache reads (any host memory; caller-owned, must
+ * outlive the executor).  bytes must equal E * row_bytes.  Errors: OES_ERR_ARG. */
+oes_status oes_cpu_moe_set_source(oes_cpu_moe *m, int32_t bank, int32_t layer, const void *host, int64_t bytes);
+
+/* The CPU part of a hybrid step: for every pair (t, j) with slot_ids[t, j] < 0,
+ * expert e = ids[t, j] of `layer`:
+ *   h = silu(Wg_e . x_t) * (Wu_e . x_t)   (fp32, rounded to bf16)
+ *   y[t] += w[t, j] * (Wd_e . h)           (fp32, pairs in (t, j) order)
+ * y rows of tokens with no such pair are 0.  x bf16 [n, H], ids and slot_ids
+ * int32 [n, k], w fp32 [n, k], y fp32 [n, H]; all host, row-major.  Results
+ * do not depend on the thread count.  Errors: OES_ERR_ARG (range, an id of a
+ * CPU pair outside [0, E), a bank of the layer without a source). */
+oes_status oes_cpu_moe_run(oes_cpu_moe *m, int32_t layer, const void *x_bf16, const int32_t *ids,
+                           const int32_t *slot_ids, const float *w, int32_t n, int32_t k, float *y);
+
+/* DRAM read ceiling (benchmark guide §5.2: a STREAM-style read): every byte of
+ * the host buffer read once by the executor's threads; *ms = wall time. */
+oes_status oes_cpu_moe_probe_read(oes_cpu_moe *m, const void *buf, int64_t bytes, double *ms);
+
+/* Backend decision of benchmark guide §5.2 and fetch split of §5.4:
+ * *hybrid = 1 iff the format has a CPU path and cpu_gbps > threshold *
+ * pcie_gbps (the page's default threshold is 2); *fetch_fraction = pcie_gbps /
+ * cpu_gbps, or 1 when the CPU is no faster (the hybrid_fetch_fraction that
+ * oes_ensure_experts_hybrid takes).  Errors: OES_ERR_ARG (pcie_gbps <= 0,
+ * cpu_gbps < 0, threshold <= 0, NaN). */
+oes_status oes_hybrid_decide(int32_t format, double cpu_gbps, double pcie_gbps, double threshold,
+                             int32_t *hybrid, double *fetch_fraction);
+
+/* One hybrid MoE layer step (benchmark guide §5.4, architecture walk-through
+ * §5): oes_ensure_experts_hybrid with (max_fetch, fetch_fraction); the step's
+ * x, ids, slot_ids and w copied to `host_ws`; copy_missing and expert_ffn
+ * enqueued on `stream` (the GPU computes the fetched and resident experts,
+ * skipping the -1 pairs); the host waits only for the small copies, then runs
+ * oes_cpu_moe_run on the -1 pairs while the GPU copies and computes; the CPU
+ * result goes to `dev_ws` and is added into y (oes_combine_cpu), after the FFN
+ * in stream order.  Returns once the CPU part is done and the rest is
+ * enqueued.  x bf16 [n, H], ids int32 [n, k], w fp32 [n, k], slot_ids int32
+ * [n, k] (written), y bf16 [n, H] and the FFN workspace are device buffers as
+ * for the separate calls; host_ws must be pinned host memory (hipHostMalloc /
+ * torch pin_memory) of at least the size oes_hybrid_workspace gives, dev_ws
+ * device memory of its size; both are reused by the next step on the same
+ * stream.  `cpu` must have the cache's schema and sources.  Errors: those of
+ * the calls it makes, OES_ERR_ARG (workspace sizes, schema mismatch). */
+oes_status oes_hybrid_workspace(const oes_cache *c, int32_t n, int32_t k, int64_t *host_bytes, int64_t *dev_bytes);
+oes_status oes_hybrid_step(oes_cache *c, oes_cpu_moe *cpu, int32_t layer, const void *x, const int32_t *ids,
+                           const float *w, int32_t n, int32_t k, int32_t *slot_ids, void *y, void *ffn_ws,
+                           int64_t ffn_ws_bytes, void *host_ws, int64_t host_ws_bytes, void *dev_ws,
+                           int64_t dev_ws_bytes, int32_t max_fetch, double fetch_fraction, void *stream);
+
+/* y_bf16[i] = bf16_rne(float(y_bf16[i]) + y_cpu[i]) for i < count: adds the
+ * executor's output (copied to the device) into the GPU FFN's output of the
+ * same step.  Device pointers; enqueued on `stream`. */
+oes_status oes_combine_cpu(void *y_bf16, const float *y_cpu, int64_t count, void *stream);
+
 /* Decode `n` elements of type `elem` (OES_ELEM_E4M3, OES_ELEM_FP4X2,
  * OES_ELEM_E8M0, OES_ELEM_BF16, OES_ELEM_FP16, OES_ELEM_Q4X2) from device
  * `codes` into device float `out` with the same device routines the FFN

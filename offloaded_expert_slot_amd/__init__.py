@@ -13,6 +13,8 @@ The names follow the C ABI in ``include/oes.h``:
                                                .ensure_experts / .copy_missing / .expert_ffn / .resize
     route(x, wg, k, ...) / route_logits(logits, k, ...)
     Layers(schema, depth, device)              .set_source / .prefetch / .ffn
+    CpuMoe(schema, threads)                    .set_source / .run   (hybrid backend, host)
+    hybrid_decide(format, cpu, pcie) / combine_cpu(y, y_cpu)
 """
 import ctypes
 import os
@@ -116,6 +118,18 @@ _SIGS = {
     "oes_probe_mfma_bf16": (_I32, [_I32, _I32, _P, _P, _PF, ctypes.POINTER(ctypes.c_double)]),
     "oes_debug_decode": (_I32, [_I32, _P, _I32, _P, _P]),
     "oes_cache_resize": (_I32, [_P, _I32, _P]),
+    "oes_cpu_moe_create": (_I32, [ctypes.POINTER(Schema), _I32, ctypes.POINTER(_P)]),
+    "oes_cpu_moe_destroy": (_I32, [_P]),
+    "oes_cpu_moe_threads": (_I32, [_P, _PI32]),
+    "oes_cpu_moe_set_source": (_I32, [_P, _I32, _I32, _P, _I64]),
+    "oes_cpu_moe_run": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _P]),
+    "oes_cpu_moe_probe_read": (_I32, [_P, _P, _I64, ctypes.POINTER(ctypes.c_double)]),
+    "oes_hybrid_decide": (_I32, [_I32, ctypes.c_double, ctypes.c_double, ctypes.c_double, _PI32,
+                                 ctypes.POINTER(ctypes.c_double)]),
+    "oes_combine_cpu": (_I32, [_P, _P, _I64, _P]),
+    "oes_hybrid_workspace": (_I32, [_P, _I32, _I32, _PI64, _PI64]),
+    "oes_hybrid_step": (_I32, [_P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _I64, _P, _I64, _I32,
+                               ctypes.c_double, _P]),
 }
 
 
@@ -299,6 +313,21 @@ class Cache:
         _check(lib().oes_ensure_experts_hybrid(self._h, layer, _ptr(ids), n, k, _ptr(slot_ids), int(max_fetch),
                                                float(fetch_fraction), _stream(stream)))
 
+    def hybrid_workspace(self, n, k):
+        """(pinned host bytes, device bytes) a hybrid step of n tokens needs."""
+        hb, db = _I64(), _I64()
+        _check(lib().oes_hybrid_workspace(self._h, n, k, ctypes.byref(hb), ctypes.byref(db)))
+        return hb.value, db.value
+
+    def hybrid_step(self, cpu, layer, x, ids, w, slot_ids, y, ffn_ws, host_ws, dev_ws, max_fetch=-1,
+                    fetch_fraction=-1.0, stream=None):
+        """ensure_experts_hybrid + copy + GPU FFN, the -1 experts on the CPU executor, combined into y."""
+        n, k = ids.shape
+        _check(lib().oes_hybrid_step(self._h, cpu._h, layer, _ptr(x), _ptr(ids), _ptr(w), n, k, _ptr(slot_ids),
+                                     _ptr(y), _ptr(ffn_ws), ffn_ws.numel(), _ptr(host_ws), host_ws.numel(),
+                                     _ptr(dev_ws), dev_ws.numel(), int(max_fetch), float(fetch_fraction),
+                                     _stream(stream)))
+
     def copy_missing(self, stream=None):
         _check(lib().oes_copy_missing(self._h, _stream(stream)))
 
@@ -376,6 +405,63 @@ class Layers:
         n, k = ids.shape
         _check(lib().oes_layers_ffn(self._h, layer, _ptr(x), _ptr(ids), _ptr(w), n, k, _ptr(y), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class CpuMoe:
+    """CPU MoE executor of the hybrid backend (oes_cpu_moe_*): host tensors only."""
+
+    def __init__(self, schema, threads=0):
+        self.schema = schema
+        h = _P()
+        _check(lib().oes_cpu_moe_create(ctypes.byref(schema), int(threads), ctypes.byref(h)))
+        self._h = h
+        self._sources = {}
+
+    def close(self):
+        if self._h:
+            _check(lib().oes_cpu_moe_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def threads(self):
+        n = _I32()
+        _check(lib().oes_cpu_moe_threads(self._h, ctypes.byref(n)))
+        return n.value
+
+    def set_source(self, bank, layer, host_tensor):
+        _check(lib().oes_cpu_moe_set_source(self._h, bank, layer, _ptr(host_tensor),
+                                            host_tensor.numel() * host_tensor.element_size()))
+        self._sources[(bank, layer)] = host_tensor  # keep alive
+
+    def run(self, layer, x, ids, slot_ids, w, y):
+        """y[n, H] fp32 = the experts of the pairs with slot_ids < 0 (host tensors or arrays)."""
+        n, k = ids.shape
+        _check(lib().oes_cpu_moe_run(self._h, layer, _ptr(x), _ptr(ids), _ptr(slot_ids), _ptr(w), n, k, _ptr(y)))
+
+    def probe_read(self, buf, nbytes):
+        """Wall ms of reading nbytes of a host buffer with every thread."""
+        ms = ctypes.c_double()
+        _check(lib().oes_cpu_moe_probe_read(self._h, _ptr(buf), int(nbytes), ctypes.byref(ms)))
+        return ms.value
+
+
+def hybrid_decide(fmt, cpu_gbps, pcie_gbps, threshold=2.0):
+    """(use hybrid?, fetch fraction) of the measured bandwidths (oes_hybrid_decide)."""
+    h, f = _I32(), ctypes.c_double()
+    _check(lib().oes_hybrid_decide(FORMAT_IDS.get(fmt, fmt), float(cpu_gbps), float(pcie_gbps), float(threshold),
+                                   ctypes.byref(h), ctypes.byref(f)))
+    return bool(h.value), f.value
+
+
+def combine_cpu(y, y_cpu, stream=None):
+    """y (bf16 bits, device) += y_cpu (fp32, device), rounded to bf16."""
+    _check(lib().oes_combine_cpu(_ptr(y), _ptr(y_cpu), y.numel(), _stream(stream)))
 
 
 def debug_decode(elem, codes, n, out, stream=None):

@@ -34,6 +34,18 @@ oes_status fail(oes_status st, const char *fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+namespace oes {
+// Leaves msg in the thread-local error string (for the host-only sources).
+oes_status set_error(oes_status st, const char *msg) {
+  g_err = msg;
+  return st;
+}
+}  // namespace oes
+
+namespace {
+
 oes_status hip_fail(hipError_t e, const char *what) {
   (void)hipGetLastError();  // clear the runtime's sticky last-error slot
   return fail(OES_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -173,6 +185,7 @@ struct oes_cache {
   int fused_copy = 1, copy_mode = OES_COPY_ZERO, copy_blocks = 0;
   uint8_t *snap = nullptr;  // device snapshot: owner | stamp | clock
   bool has_snap = false;
+  hipEvent_t hybrid_ev = nullptr;  // hybrid step: the step's ids have reached the host
 };
 
 struct oes_layers {
@@ -355,6 +368,7 @@ static void cache_free(oes_cache *c) {
   if (c->snap) (void)hipFree(c->snap);
   if (c->staging) (void)hipHostFree(c->staging);
   if (c->staging_done) (void)hipEventDestroy(c->staging_done);
+  if (c->hybrid_ev) (void)hipEventDestroy(c->hybrid_ev);
   c->src.release();
   delete c;
 }
@@ -1221,6 +1235,93 @@ extern "C" oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *s
   HIP_TRY(hipEventRecord(e1, s));
   *flops = (double)mfma_probe_flops(blocks, iters);
   return timed(s, ms, e0, e1);
+}
+
+// ============================================================================ hybrid step
+namespace oes {
+const oes_schema *cpu_moe_schema(const oes_cpu_moe *m);  // cpu_moe.cpp
+}
+
+// Host workspace of a hybrid step: x bf16 [n, H] | ids | slot_ids | w [n, k] | y_cpu fp32 [n, H].
+struct HybridHost {
+  int64_t x, ids, slots, w, y, total;
+};
+static HybridHost hybrid_host_layout(int64_t n, int64_t k, int64_t H) {
+  HybridHost l;
+  int64_t off = 0;
+  l.x = off;     off = round_up(off + 2 * n * H, 64);
+  l.ids = off;   off = round_up(off + 4 * n * k, 64);
+  l.slots = off; off = round_up(off + 4 * n * k, 64);
+  l.w = off;     off = round_up(off + 4 * n * k, 64);
+  l.y = off;     off = round_up(off + 4 * n * H, 64);
+  l.total = off;
+  return l;
+}
+
+extern "C" oes_status oes_hybrid_workspace(const oes_cache *c, int32_t n, int32_t k, int64_t *host_bytes,
+                                           int64_t *dev_bytes) {
+  if (!c || !host_bytes || !dev_bytes) return fail(OES_ERR_ARG, "NULL argument");
+  if (n < 0 || k < 1) return fail(OES_ERR_ARG, "need n >= 0 and k >= 1");
+  *host_bytes = hybrid_host_layout(n, k, c->sc.hidden).total;
+  *dev_bytes = round_up(4ll * n * c->sc.hidden, 64);
+  return OES_OK;
+}
+
+extern "C" oes_status oes_hybrid_step(oes_cache *c, oes_cpu_moe *cpu, int32_t layer, const void *x,
+                                      const int32_t *ids, const float *w, int32_t n, int32_t k, int32_t *slot_ids,
+                                      void *y, void *ffn_ws, int64_t ffn_ws_bytes, void *host_ws,
+                                      int64_t host_ws_bytes, void *dev_ws, int64_t dev_ws_bytes,
+                                      int32_t max_fetch, double fetch_fraction, void *stream) {
+  if (!c || !cpu) return fail(OES_ERR_ARG, "cache or executor is NULL");
+  if (memcmp(oes::cpu_moe_schema(cpu), &c->sc, sizeof(oes_schema)) != 0)
+    return fail(OES_ERR_ARG, "the executor and the cache have different schemas");
+  if (n < 0 || k < 1 || k > 32) return fail(OES_ERR_ARG, "need n >= 0 and 1 <= k <= 32");
+  if (n == 0) return OES_OK;
+  if (!x || !ids || !w || !slot_ids || !y || !host_ws || !dev_ws) return fail(OES_ERR_ARG, "NULL buffer");
+  const int H = c->sc.hidden;
+  const HybridHost l = hybrid_host_layout(n, k, H);
+  if (host_ws_bytes < l.total) return fail(OES_ERR_ARG, "host workspace %lld < %lld bytes", (long long)host_ws_bytes, (long long)l.total);
+  if (dev_ws_bytes < 4ll * n * H) return fail(OES_ERR_ARG, "device workspace %lld < %lld bytes", (long long)dev_ws_bytes, 4ll * n * H);
+  DeviceGuard g(c->device);
+  if (!g.ok) return fail(OES_ERR_HIP, "hipSetDevice(%d) failed", c->device);
+  hipStream_t s = as_stream(stream);
+  if (!c->hybrid_ev) HIP_TRY(hipEventCreateWithFlags(&c->hybrid_ev, hipEventDisableTiming));
+  uint8_t *hw = static_cast<uint8_t *>(host_ws);
+  // 1. the remap, and the step's routing on its way to the host
+  oes_status st = oes_ensure_experts_hybrid(c, layer, ids, n, k, slot_ids, max_fetch, fetch_fraction, stream);
+  if (st != OES_OK) return st;
+  HIP_TRY(hipMemcpyAsync(hw + l.x, x, 2 * (size_t)n * H, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(hw + l.ids, ids, 4 * (size_t)n * k, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(hw + l.slots, slot_ids, 4 * (size_t)n * k, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(hw + l.w, w, 4 * (size_t)n * k, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipEventRecord(c->hybrid_ev, s));
+  // 2. the GPU part: fetch the capped misses, FFN over the slot pairs (-1 pairs skipped)
+  st = oes_copy_missing(c, stream);
+  if (st != OES_OK) return st;
+  st = oes_expert_ffn(c, x, slot_ids, w, n, k, y, ffn_ws, ffn_ws_bytes, stream);
+  if (st != OES_OK) return st;
+  // 3. the CPU part, while the GPU copies
+  HIP_TRY(hipEventSynchronize(c->hybrid_ev));
+  const int32_t *hs = reinterpret_cast<const int32_t *>(hw + l.slots);
+  bool any = false;
+  for (int64_t i = 0; i < (int64_t)n * k; ++i) any = any || hs[i] < 0;
+  if (!any) return OES_OK;
+  float *yc = reinterpret_cast<float *>(hw + l.y);
+  st = oes_cpu_moe_run(cpu, layer, hw + l.x, reinterpret_cast<const int32_t *>(hw + l.ids), hs,
+                       reinterpret_cast<const float *>(hw + l.w), n, k, yc);
+  if (st != OES_OK) return st;
+  // 4. y += y_cpu, after the GPU FFN in stream order
+  HIP_TRY(hipMemcpyAsync(dev_ws, yc, 4 * (size_t)n * H, hipMemcpyHostToDevice, s));
+  HIP_TRY(launch_add_to_bf16(static_cast<uint16_t *>(y), static_cast<const float *>(dev_ws), (int64_t)n * H, s));
+  return OES_OK;
+}
+
+extern "C" oes_status oes_combine_cpu(void *y_bf16, const float *y_cpu, int64_t count, void *stream) {
+  if (count < 0) return fail(OES_ERR_ARG, "count < 0");
+  if (count == 0) return OES_OK;
+  if (!y_bf16 || !y_cpu) return fail(OES_ERR_ARG, "NULL buffer");
+  HIP_TRY(launch_add_to_bf16(static_cast<uint16_t *>(y_bf16), y_cpu, count, as_stream(stream)));
+  return OES_OK;
 }
 
 extern "C" oes_status oes_debug_decode(int32_t elem, const void *codes, int32_t n, float *out, void *stream) {

@@ -1,4 +1,5 @@
-"""Build liboes.so for gfx950 with hipcc (in-tree, next to the Python binding).
+"""Build liboes.so for gfx950 with hipcc (in-tree, next to the Python binding); the
+host-only CPU MoE executor is compiled with g++ and linked in.
 
 Usage: python -m offloaded_expert_slot_amd.csrc.build  [--jobs N]
 """
@@ -11,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-SOURCES = ["api.hip", "k_lru.hip", "k_copy.hip", "k_route.hip", "k_ffn.hip", "k_prefill.hip"]
+SOURCES = ["api.hip", "k_lru.hip", "k_copy.hip", "k_route.hip", "k_ffn.hip", "k_prefill.hip", "cpu_moe.cpp"]
 OUT = os.path.join(PKG, "liboes.so")
 BUILD = os.path.join(HERE, "_build")
 
@@ -25,9 +26,17 @@ FLAGS = [
 ]
 
 
+# host-only sources (the CPU MoE executor): g++, AVX-512 code behind per-function target attributes
+CXX = os.environ.get("CXX", "g++")
+CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXX_FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -44,7 +53,7 @@ def build(jobs=None, verbose=False):
         if verbose and warn:
             print(f"[{src}]\n{warn}", file=sys.stderr)
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", "-pthread", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

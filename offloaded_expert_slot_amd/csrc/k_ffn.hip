@@ -631,7 +631,19 @@ __global__ void debug_decode_kernel(int elem, const uint8_t *codes, int n, float
   }
 }
 
+// ------------------------------------------------------------------ hybrid combine
+__global__ __launch_bounds__(256) void add_to_bf16_kernel(uint16_t *y, const float *add, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = f32_to_bf16_rne(bf16_to_f32(y[i]) + add[i]);
+}
+
 }  // namespace
+
+hipError_t launch_add_to_bf16(uint16_t *y, const float *add, int64_t count, hipStream_t s) {
+  const int blocks = (int)std::min<int64_t>(1024, (count + 255) / 256);
+  hipLaunchKernelGGL(add_to_bf16_kernel, dim3(blocks), dim3(256), 0, s, y, add, count);
+  return hipGetLastError();
+}
 
 bool expert_ffn_supported(int format, int H, int I, int k) {
   const int epc = epc_of(format);

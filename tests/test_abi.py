@@ -84,3 +84,18 @@ def test_null_and_range_errors_without_gpu(L):
 def test_header_lists_binding_functions():
     # every binding entry is declared in the header (no private entry points)
     assert set(oes._SIGS) == set(oes.header_functions())
+
+
+def test_hybrid_decide_matches_the_oracle_rule():
+    """oes_hybrid_decide is host logic: the backend choice and the fetch fraction
+    equal the oracle's (benchmark guide §5.2 and §5.4) on a grid of bandwidths."""
+    from oracle import formulas
+    for fmt in ("bf16", "nvfp4", "q4_0", "fp8_block128", "mxfp4_t"):
+        for cpu in (0.0, 20.0, 56.0, 111.9, 112.0, 112.1, 300.0):
+            for pcie in (28.0, 56.0):
+                for thr in (1.0, 2.0, 3.0):
+                    hyb, frac = oes.hybrid_decide(fmt, cpu, pcie, thr)
+                    assert hyb == (formulas.recommend_backend(fmt, cpu, pcie, thr) == "hybrid")
+                    assert frac == formulas.hybrid_fetch_fraction(pcie, cpu)
+    with pytest.raises(oes.OesError):
+        oes.hybrid_decide("bf16", 10.0, 0.0)

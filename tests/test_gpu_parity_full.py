@@ -286,3 +286,46 @@ def test_resize_full_size():
     assert np.array_equal(d_slots.cpu().numpy(), r.slot_ids)
     assert c.get_misses() == r.misses
     c.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,bs,frac", [("bf16_h2048", 1, 0.5), ("bf16_h2048", 8, 0.3), ("q4_0_h2048", 4, 0.5)])
+def test_hybrid_layer_step_full_size(name, bs, frac):
+    """The hybrid layer step at full size (every slot foreign, so every routed
+    expert misses): fetched experts on the GPU, the rest on the CPU executor;
+    y equals the oracle FFN over every routed pair (tokens sampled)."""
+    w, hb, c = _setup(name)
+    _case(f"hybrid layer step {name} bs={bs} frac={frac}")
+    dev = G.dev()
+    sc = oes.schema_make(w.fmt, w.L, w.E, w.H, w.I)
+    cpu = oes.CpuMoe(sc, 0)
+    for b, t in enumerate(hb.banks):
+        cpu.set_source(b, 0, t)
+    x = synth.activations(bs, w.H, 0, w.name, step=11).to(dev)
+    wg = synth.router_weight(w.H, w.E, 0, w.name).to(dev)
+    oids, ow, _ = oroute.route(G.bits16(x), G.bits16(wg), w.k)
+    ids = torch.from_numpy(oids).to(dev)
+    wts = torch.from_numpy(ow.astype(np.float32)).to(dev)
+    owner, stamp, clock = synth.foreign_state(w.S, w.E)
+    c.set_state(owner, stamp, clock)
+    slot_ids = torch.empty_like(ids)
+    y = torch.empty((bs, w.H), dtype=torch.int16, device=dev)
+    hws, dws = c.hybrid_workspace(bs, w.k)
+    host_ws = torch.empty(hws, dtype=torch.uint8, pin_memory=True)
+    dev_ws = torch.empty(dws, dtype=torch.uint8, device=dev)
+    ffn_ws = torch.empty(c.ffn_workspace_bytes(bs, w.k), dtype=torch.uint8, device=dev)
+    c.hybrid_step(cpu, 0, x, ids, wts, slot_ids, y, ffn_ws, host_ws, dev_ws, -1, frac)
+    torch.cuda.synchronize()
+    c.check()
+    t = SlotTable(w.S, w.L, w.E)
+    t.set_state(owner, stamp, clock)
+    r = t.ensure_hybrid(0, oids, -1, frac)
+    assert np.array_equal(slot_ids.cpu().numpy(), r.slot_ids)
+    assert len(r.overflow) > 0 and r.num_indices + len(r.overflow) == r.num_missing_full
+    sel = [0] if bs == 1 else [0, bs - 1]
+    ref = offn.expert_ffn(w.fmt, w.H, w.I, G.bits16(x)[sel], oids[sel], ow[sel].astype(np.float32).astype(np.float64),
+                          lambda e: [hb.row(b, int(e)).numpy() for b in range(len(hb.banks))])
+    err = offn.rel_l2(G.bf16_tensor_to_f64(y)[sel], ref)
+    print(f"  rel_l2={err:.3e} fetched={r.num_indices} cpu={len(r.overflow)}")
+    assert err <= (3e-2 if w.fmt in ("nvfp4", "q4_0") else 1e-2)
+    cpu.close()
