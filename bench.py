@@ -20,7 +20,10 @@ Also printed (same JSON line): the copy sweep of the benchmark guide's columns
 25 event-timed ensure+copy repeats, fused and per-bank), decode tok/s at every
 miss rate, the measured ceilings (pinned H2D by DMA and by the zero-copy
 kernel, HBM streaming read, bf16 MFMA loop), the roofline of the dominant kernel and of the
-FFN, the cold decode FFN of every decode bank format (bf16, fp8 block, nvfp4,
+FFN, the hybrid backend (host DRAM read and link ceilings, the CPU MoE
+executor and the PCIe gather alone and overlapped, the decision and fetch
+split, the hybrid decode layer step beside the offload one), the cold decode
+FFN of every decode bank format (bf16, fp8 block, nvfp4,
 GGUF Q4_0) at its workload's shape, a slot-pool resize (half the slots and back),
 the MXFP4 prefill layer (grouped FFN on MFMA, whole-layer stream, the
 overlapped loop over 4 layers) and the CPU oracle timed on this host.
@@ -55,6 +58,8 @@ def parse():
     ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill (MXFP4 layer stream) part")
+    ap.add_argument("--no-hybrid", action="store_true", help="skip the hybrid backend (CPU executor) part")
+    ap.add_argument("--hybrid-steps", type=int, default=20, help="timed hybrid / synced offload layer steps")
     return ap.parse_args()
 
 
@@ -269,6 +274,11 @@ def main():
         cache.set_option(oes.OPT_FUSED_COPY, 1)
         cache.check()
 
+    # ---------------------------------------------------------------- hybrid backend (ft bench bw + the hybrid step)
+    hybrid = None
+    if not args.no_hybrid:
+        hybrid = _hybrid(cache, hb, w, bpe, x, wg, rws, fws, prepare, probes, per_mr, args, log)
+
     # ---------------------------------------------------------------- slot-pool resize
     resize = _resize(cache, w, bpe, log)
 
@@ -323,10 +333,143 @@ def main():
                    "misses": head["misses"], "active": active, "bytes_per_expert": bpe},
         "tok_ms": head["tok_ms"], "copy_GBps": head.get("copy_GBps"),
         "roofline": roof, "kernels": kernels, "probes": probes, "decode_per_miss_rate": per_mr,
-        "copy_sweep": sweep, "ffn_formats": ffn_formats, "resize": resize, "prefill": prefill, "cpu_baseline": cpu,
+        "copy_sweep": sweep, "ffn_formats": ffn_formats, "hybrid": hybrid, "resize": resize, "prefill": prefill,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     cache.close()
+
+
+def _hybrid(cache, hb, w, bpe, x, wg, rws, fws, prepare, probes, per_mr, args, log):
+    """The hybrid backend on the bench workload (benchmark guide §5.2-§5.4).
+
+    ft bench bw: the DRAM read ceiling (every host bank byte read once by the
+    executor's threads) beside the pinned H2D ceiling; the real kernels - the
+    CPU executor on k experts of one token (every pair left to the CPU) and the
+    PCIe gather of k misses - alone, then overlapped (the gather of k experts
+    enqueued, the executor run on k others meanwhile); the decision (alone
+    bandwidths) and the fetch fraction (overlapped ones).
+
+    Then the decode layer step at bs=1 and the headline miss rate, hybrid
+    (route, then oes_hybrid_step with that fraction) and offload (route,
+    ensure, copy, FFN), both timed by wall clock from the route launch to y on
+    the host side of a stream sync, since the hybrid step itself waits for the
+    remap; the slot table is restored (untimed) before every step.
+    """
+    import numpy as np
+    import torch
+
+    import offloaded_expert_slot_amd as oes
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sc = oes.schema_make(w.fmt, w.L, w.E, w.H, w.I)
+    cpu = oes.CpuMoe(sc, 0)
+    for b, t in enumerate(hb.banks):
+        cpu.set_source(b, 0, t)
+    out = {"threads": cpu.threads, "format": w.fmt}
+
+    # ceilings
+    host_bytes = sum(t.numel() for t in hb.banks)
+    reads = [cpu.probe_read(t, t.numel()) for t in hb.banks for _ in range(3)]
+    per_bank = [min(reads[3 * b:3 * b + 3]) for b in range(len(hb.banks))]
+    out["dram_read_GBps"] = host_bytes / (sum(per_bank) * 1e6)
+    out["h2d_GBps"] = probes.get("h2d_peak_GBps") if probes else None
+
+    # real kernels, alone: k experts per call, rotating over E / k disjoint sets
+    k, E = w.k, w.E
+    sets = [np.arange(i * k, (i + 1) * k, dtype=np.int32).reshape(1, k) for i in range(E // k)]
+    xh = synth.activations(1, w.H, 0, w.name)
+    allcpu = np.full((1, k), -1, dtype=np.int32)
+    wk = np.full((1, k), 1.0 / k, dtype=np.float32)
+    yc = np.zeros((1, w.H), dtype=np.float32)
+    for i in range(3):
+        cpu.run(0, xh, sets[i], allcpu, wk, yc)
+    times = []
+    for i in range(12):
+        t0 = time.perf_counter()
+        cpu.run(0, xh, sets[(3 + i) % len(sets)], allcpu, wk, yc)
+        times.append(time.perf_counter() - t0)
+    cpu_ms = float(np.median(times)) * 1e3
+    out["cpu_moe_ms"] = cpu_ms
+    out["cpu_moe_GBps"] = k * bpe / (cpu_ms * 1e6)
+    full = [r for r in per_mr if r["miss_rate"] == 1.0 and r.get("copy_GBps")]
+    out["pcie_gather_GBps"] = full[0]["copy_GBps"] if full else None
+
+    # overlapped: the gather of k misses (every slot foreign) with the executor on k other experts
+    owner, stamp, clock = synth.foreign_state(w.S, w.E)
+    d_ids = [torch.from_numpy(sets[i]).to(dev) for i in range(len(sets))]
+    d_slots = torch.empty((1, k), dtype=torch.int32, device=dev)
+    gpu_ms, cpu_ov = [], []
+    for i in range(8):
+        cache.set_state(owner, stamp, clock)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cache.ensure_experts(0, d_ids[i % len(sets)], d_slots)
+        cache.copy_missing()
+        b.record(stream)
+        t0 = time.perf_counter()
+        cpu.run(0, xh, sets[(i + len(sets) // 2) % len(sets)], allcpu, wk, yc)
+        cpu_ov.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        gpu_ms.append(a.elapsed_time(b))
+    cache.check()
+    out["overlap_cpu_GBps"] = k * bpe / (float(np.median(cpu_ov)) * 1e9)
+    out["overlap_pcie_GBps"] = k * bpe / (float(np.median(gpu_ms)) * 1e6)
+    pcie = out["pcie_gather_GBps"] or out["overlap_pcie_GBps"]
+    use, _ = oes.hybrid_decide(w.fmt, out["cpu_moe_GBps"], pcie)
+    _, frac = oes.hybrid_decide(w.fmt, out["overlap_cpu_GBps"], out["overlap_pcie_GBps"])
+    out["decision"] = "hybrid" if use else "offload"
+    out["fetch_fraction"] = frac
+
+    # the decode layer step, hybrid vs offload, wall clock with a sync per step
+    mr = args.miss_rate
+    misses, owner, stamp, clock, pre = prepare(mr)
+    cache.set_state(owner, stamp, clock)
+    if pre:
+        cache.load_rows([p[0] for p in pre], [p[1] for p in pre])
+    cache.snapshot()
+    x1 = x[:1]
+    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, k), dtype=torch.float32, device=dev)
+    slot_ids = torch.empty_like(ids)
+    y = torch.empty((1, w.H), dtype=torch.int16, device=dev)
+    hws, dws = cache.hybrid_workspace(1, k)
+    host_ws = torch.empty(hws, dtype=torch.uint8, pin_memory=True)
+    dev_ws = torch.empty(dws, dtype=torch.uint8, device=dev)
+
+    def step(kind):
+        cache.restore()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        oes.route(x1, wg, k, ids, wts, rws)
+        if kind == "hybrid":
+            cache.hybrid_step(cpu, 0, x1, ids, wts, slot_ids, y, fws, host_ws, dev_ws, -1, frac)
+        else:
+            cache.ensure_experts(0, ids, slot_ids)
+            cache.copy_missing()
+            cache.expert_ffn(x1, slot_ids, wts, y, fws)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    res = {}
+    for kind in ("offload", "hybrid"):
+        for _ in range(3):
+            step(kind)
+        ts = [step(kind) for _ in range(args.hybrid_steps)]
+        ms = float(np.median(ts)) * 1e3
+        res[kind] = {"ms_per_step": ms, "decode_tok_s": 1000.0 / (w.L * ms)}
+    cache.check()
+    st = cache.stats()
+    res["hybrid"]["fetched_last_step"] = st["last_indices"]
+    res["hybrid"]["cpu_experts_last_step"] = st["last_missing_full"] - st["last_indices"]
+    out.update({"miss_rate": mr, "misses": misses, "step": res,
+                "hybrid_speedup": res["offload"]["ms_per_step"] / res["hybrid"]["ms_per_step"]})
+    log("hybrid", {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in out.items() if kk != "step"}, res)
+    cpu.close()
+    return out
 
 
 def _resize(cache, w, bpe, log):
