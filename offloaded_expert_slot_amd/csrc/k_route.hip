@@ -10,10 +10,10 @@
 //                    (a 16-byte load per row, coalesced along E) and up to 16
 //                    rows whose loads are all issued before the first multiply.
 //   route_finish   - one workgroup per token: all threads sum the partials
-//                    (deterministic order), then one wave writes the logits,
-//                    picks the top-k by repeated wave argmax (larger logit
-//                    first, lower index on ties) and the softmax over the
-//                    chosen logits.
+//                    (deterministic order) and write the logits; each expert's
+//                    rank (experts with a larger logit, or an equal one at a
+//                    lower index) picks the top-k in order; one wave takes the
+//                    softmax over the chosen logits.
 // route_logits runs route_finish alone on given logits (one split).
 
 #include <math.h>
@@ -31,6 +31,7 @@ constexpr int kRpt = 16;        // rows per thread, all loads issued at once
 constexpr int kMaxTok = 32;     // tokens per pass of the partial kernel
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
@@ -114,27 +115,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_partial_kernel(const uint
   }
 }
 
-struct Cand {
-  float v;
-  int i;
-};
-
-__device__ inline bool better(const Cand &a, const Cand &b) {  // a ranks before b
-  return a.v > b.v || (a.v == b.v && a.i < b.i);
-}
-
-constexpr int kMaxPerLane = 8;  // E <= 512 experts over 64 lanes
-
 // One workgroup per token.  All 256 threads sum the split partials (thread i
 // takes expert i % E and splits i / E, i / E + 256 / E, ... with independent
 // loads; the per-thread sums are added in a fixed order through LDS, so the
-// result is deterministic).  Then wave 0 picks the top-k by k rounds of a wave
-// argmax (larger logit first, lower index on ties); lane j keeps the j-th pick
-// and writes its id and renormalised weight.
+// result is deterministic).  Then the top-k by rank (larger logit first, lower
+// index on ties); lane j of wave 0 takes the j-th pick and writes its id and
+// renormalised weight.
 __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float *partial, int splits, int n, int E,
                                                                      int k, float *logits, int32_t *ids, float *w) {
   __shared__ float zsum[kRouteThreads];
   __shared__ float z[512];
+  __shared__ float top_v[32];
+  __shared__ int top_i[32];
+  __shared__ __align__(16) uint64_t rkey[512 + 2];
+  __shared__ int rcnt[512];
   const int t = blockIdx.x;
   const int64_t stride = (int64_t)n * E;
   const int per = kRouteThreads / E >= 1 ? kRouteThreads / E : 1;   // threads per expert (E <= 256)
@@ -180,40 +174,55 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float
     }
   }
   __syncthreads();
+  // top-k by rank: expert e's rank is the number of experts that beat it - a larger
+  // logit, or an equal one at a lower index; a NaN logit is beaten by every number
+  // and NaNs among themselves go by index.  Each expert gets one 64-bit key that
+  // orders exactly so (the logit mapped to an order-preserving integer, -0 as +0
+  // and NaN below -inf, then the inverted index), so the ranks are a permutation
+  // and rank(e) = #{q : key[q] > key[e]}; the k experts of rank < k are the
+  // picks, in order.  Each expert's count is split over up to 256 / E threads
+  // that read two keys per 16-byte LDS load.
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    float v = z[e];
+    if (v == 0.f) v = 0.f;
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t ord = v != v ? 0u : ((u >> 31) ? ~u : (u | 0x80000000u));
+    rkey[e] = ((uint64_t)ord << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+  }
+  if ((E & 1) && threadIdx.x == 0) rkey[E] = 0;  // pad to an even count: beats nothing
+  __syncthreads();
+  {
+    const int parts = E <= kRouteThreads / 2 ? kRouteThreads / E : 1;
+    const int E2 = (E + 1) / 2;                        // key pairs
+    for (int slot = threadIdx.x; slot < E * parts; slot += kRouteThreads) {
+      const int e = slot % E, part = slot / E;
+      const uint64_t ke = rkey[e];
+      const int q0 = E2 * part / parts, q1 = E2 * (part + 1) / parts;
+      const u64x2 *kp = reinterpret_cast<const u64x2 *>(rkey);
+      int cnt = 0;
+#pragma unroll 8
+      for (int q = q0; q < q1; ++q) {
+        const u64x2 kk = kp[q];
+        cnt += (kk.x > ke) + (kk.y > ke);
+      }
+      rcnt[slot] = cnt;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    const int parts = E <= kRouteThreads / 2 ? kRouteThreads / E : 1;
+    int rank = 0;
+    for (int part = 0; part < parts; ++part) rank += rcnt[part * E + e];
+    if (rank < k) {
+      top_v[rank] = z[e];
+      top_i[rank] = e;
+    }
+  }
+  __syncthreads();
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  float zl[kMaxPerLane];
-#pragma unroll
-  for (int q = 0; q < kMaxPerLane; ++q) {
-    const int e = lane + 64 * q;
-    zl[q] = e < E ? z[e] : 0.f;
-  }
-  uint32_t taken = 0;
-  float myv = 0.f;
-  int myi = 0;
-  for (int j = 0; j < k; ++j) {
-    Cand c{-INFINITY, 0x7fffffff};
-#pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q) {
-      const int e = lane + 64 * q;
-      if (e < E && !((taken >> q) & 1u)) {
-        Cand o{zl[q], e};
-        if (c.i == 0x7fffffff || better(o, c)) c = o;
-      }
-    }
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-      Cand o;
-      o.v = __shfl_xor(c.v, d, 64);
-      o.i = __shfl_xor(c.i, d, 64);
-      if (o.i != 0x7fffffff && (c.i == 0x7fffffff || better(o, c))) c = o;
-    }
-    if ((c.i & 63) == lane) taken |= 1u << (c.i >> 6);
-    if (lane == j) {
-      myv = c.v;
-      myi = c.i;
-    }
-  }
+  const float myv = lane < k ? top_v[lane] : 0.f;
+  const int myi = lane < k ? top_i[lane] : 0;
   const float v0 = __shfl(myv, 0, 64);
   const float ex = lane < k ? expf(myv - v0) : 0.f;
   float sum = ex;
