@@ -27,7 +27,10 @@
 //   khi/klo[Spad] u64  victim keys, bitonic-sorted ascending (keys live in
 //                      registers during the sort; LDS is the exchange buffer for
 //                      partners 64..kThreads-1 apart); members of U and padding
-//                      get the all-ones key and sort last.
+//                      get the all-ones key and sort last.  For up to 256
+//                      candidates (16 * registers per thread * misses) the
+//                      first `take` keys come from ranks instead (rank_victims),
+//                      with the keys as (hi, lo) pairs over the same bytes.
 // Key encoding: khi = (owner != -1) << 63 | stamp  (stamps < 2^62),
 //               klo = (owner + 1) << 12 | slot     (owner < 2^50, slot < 4096).
 
@@ -39,11 +42,12 @@ namespace oes {
 
 namespace {
 
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPerThread = OES_MAX_EXPERTS / kThreads;  // 4 experts per thread in the scan
 constexpr uint64_t kMax = ~0ull;
-constexpr int kSelectMax = 2;  // misses up to which victims are selected rather than sorted (measured crossover)
 
 // Block-wide exclusive scan of one int per thread; returns the exclusive prefix, *total the sum.
 __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
@@ -175,20 +179,26 @@ __device__ void sort_victims(const LruArgs &a, const uint8_t *req, int64_t base,
   __syncthreads();
 }
 
-// The m smallest victim keys, ascending, into khi / klo[0..m): m rounds of a
-// block-wide minimum (wave shuffles, then the 16 wave minima from LDS); the
-// thread holding the minimum drops it.  Keys are unique (the slot is in the low
-// bits), so this equals the first m entries of the full sort; for a few misses
-// it avoids sorting the whole pool.  m <= slots not holding a member of U
-// (guaranteed by the capacity check), so every selected key is a real slot.
+// The m smallest victim keys, ascending, into khi / klo[0..m), by ranks.  Group g
+// is the 64 keys of one wave and register r (slots r*kThreads + 64w + lane);
+// (1) each key's rank within its group (64 broadcast LDS reads per key); a key
+// among the m smallest of the pool is among the m smallest of its group, so
+// the keys of group rank < m (at most m per group) are the candidates;
+// (2) each candidate's rank among the candidates, counted by kThreads / C
+// threads per candidate; rank r < m goes to position r.  Keys are unique (the
+// slot is in the low bits) and padding / members of U never become
+// candidates; m <= slots not holding a member of U (the capacity check), so
+// positions 0..m-1 are all filled.  Needs 16 * R * m <= kRankCand.
+constexpr int kRankCand = 256;
+
 template <int R>
-__device__ void select_victims(const LruArgs &a, const uint8_t *req, int64_t base, int m, uint64_t *khi,
-                               uint64_t *klo, uint64_t *wmin_h, uint64_t *wmin_l) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ void rank_victims(const LruArgs &a, const uint8_t *req, int64_t base, int m, uint64_t *khi,
+                             uint64_t *klo, u64x2 *kpair, uint64_t *cand_h, uint64_t *cand_l, int *cnt) {
+  const int tid = threadIdx.x, wave = tid >> 6;
   uint64_t hi[R], lo[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int s = threadIdx.x + r * kThreads;
+    const int s = tid + r * kThreads;
     hi[r] = kMax;
     lo[r] = kMax;
     if (s < a.S) {
@@ -199,57 +209,67 @@ __device__ void select_victims(const LruArgs &a, const uint8_t *req, int64_t bas
         lo[r] = ((uint64_t)(o + 1) << 12) | (uint64_t)s;
       }
     }
+    kpair[s] = u64x2{hi[r], lo[r]};
   }
-  for (int i = 0; i < m; ++i) {
-    uint64_t bh = hi[0], bl = lo[0];
-#pragma unroll
-    for (int r = 1; r < R; ++r)
-      if (key_less(hi[r], lo[r], bh, bl)) {
-        bh = hi[r];
-        bl = lo[r];
-      }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const uint64_t ph = shfl_xor_u64(bh, d), pl = shfl_xor_u64(bl, d);
-      if (key_less(ph, pl, bh, bl)) {
-        bh = ph;
-        bl = pl;
-      }
-    }
-    if (lane == 0) {
-      wmin_h[wave] = bh;
-      wmin_l[wave] = bl;
-    }
-    __syncthreads();
-    uint64_t gh = wmin_h[0], gl = wmin_l[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-      if (key_less(wmin_h[w], wmin_l[w], gh, gl)) {
-        gh = wmin_h[w];
-        gl = wmin_l[w];
-      }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (hi[r] == gh && lo[r] == gl) {
-        hi[r] = kMax;
-        lo[r] = kMax;
-      }
-    if (threadIdx.x == 0) {
-      khi[i] = gh;
-      klo[i] = gl;
-    }
-    __syncthreads();  // the wave minima are rewritten next round
+  const int C = 16 * R * m;  // candidate slots: m per group
+  for (int c = tid; c < C; c += kThreads) {
+    cand_h[c] = kMax;
+    cand_l[c] = kMax;
   }
+  __syncthreads();
+  // (1) rank within the group
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (hi[r] == kMax && lo[r] == kMax) continue;
+    const int g0 = r * kThreads + wave * 64;
+    int rank = 0;
+#pragma unroll 8
+    for (int q = 0; q < 64; ++q) {
+      const u64x2 kq = kpair[g0 + q];
+      rank += key_less(kq.x, kq.y, hi[r], lo[r]);
+    }
+    if (rank < m) {
+      const int c = (r * 16 + wave) * m + rank;
+      cand_h[c] = hi[r];
+      cand_l[c] = lo[r];
+    }
+  }
+  __syncthreads();
+  // (2) rank among the candidates, split over `parts` threads per candidate
+  const int parts = kThreads / C;
+  for (int slot = tid; slot < C * parts; slot += kThreads) {
+    const int c = slot % C, part = slot / C;
+    const uint64_t ch = cand_h[c], cl = cand_l[c];
+    const int q0 = C * part / parts, q1 = C * (part + 1) / parts;
+    int n = 0;
+    for (int q = q0; q < q1; ++q) n += key_less(cand_h[q], cand_l[q], ch, cl);
+    cnt[slot] = n;
+  }
+  __syncthreads();
+  for (int c = tid; c < C; c += kThreads) {
+    const uint64_t ch = cand_h[c], cl = cand_l[c];
+    if (ch == kMax && cl == kMax) continue;
+    int rank = 0;
+    for (int part = 0; part < parts; ++part) rank += cnt[part * C + c];
+    if (rank < m) {
+      khi[rank] = ch;
+      klo[rank] = cl;
+    }
+  }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
-  __shared__ uint64_t khi[OES_MAX_SLOTS];
-  __shared__ uint64_t klo[OES_MAX_SLOTS];
+  // victim keys: khi / klo (sort) or interleaved pairs over the same bytes (ranks)
+  __shared__ __align__(16) uint64_t kbuf[2 * OES_MAX_SLOTS];
+  uint64_t *khi = kbuf, *klo = kbuf + OES_MAX_SLOTS;
+  u64x2 *kpair = reinterpret_cast<u64x2 *>(kbuf);
   __shared__ int32_t emap[OES_MAX_EXPERTS];
   __shared__ int32_t mrank[OES_MAX_EXPERTS];
   __shared__ uint8_t req[OES_MAX_EXPERTS];
   __shared__ int wave_tot[kWaves + 1];
-  __shared__ uint64_t wmin_h[kWaves], wmin_l[kWaves];
+  __shared__ uint64_t cand_h[kRankCand], cand_l[kRankCand];
+  __shared__ int cnt[kThreads];
   __shared__ int s_bad, s_evict;
   __shared__ uint64_t s_clock;
 
@@ -335,14 +355,15 @@ __global__ __launch_bounds__(kThreads) void lru_remap_kernel(LruArgs a) {
   }
   if (take > 0) {
     // 4-5. victim keys ascending (slots holding a member of U sort last): the
-    // first `take` of them, by selection for a few misses, else by a full sort
-    if (take <= kSelectMax) {
-      if (a.Spad <= kThreads)
-        select_victims<1>(a, req, base, take, khi, klo, wmin_h, wmin_l);
-      else if (a.Spad <= 2 * kThreads)
-        select_victims<2>(a, req, base, take, khi, klo, wmin_h, wmin_l);
+    // first `take` of them, by ranks when the candidates fit, else by a full sort
+    const int R = a.Spad <= kThreads ? 1 : (a.Spad <= 2 * kThreads ? 2 : 4);
+    if (16 * R * take <= kRankCand) {
+      if (R == 1)
+        rank_victims<1>(a, req, base, take, khi, klo, kpair, cand_h, cand_l, cnt);
+      else if (R == 2)
+        rank_victims<2>(a, req, base, take, khi, klo, kpair, cand_h, cand_l, cnt);
       else
-        select_victims<4>(a, req, base, take, khi, klo, wmin_h, wmin_l);
+        rank_victims<4>(a, req, base, take, khi, klo, kpair, cand_h, cand_l, cnt);
     } else if (a.Spad <= kThreads) {
       sort_victims<1>(a, req, base, khi, klo);
     } else if (a.Spad <= 2 * kThreads) {

@@ -81,7 +81,7 @@ def _lru_trace(S, L, E, steps, seed_state=None):
             assert c.get_misses() == r.misses, i
         else:
             assert (d_slots.cpu().numpy() == -1).all()
-            assert c.get_misses() == (misses_before if same else [])
+            assert c.get_misses() == []
     return c
 
 
