@@ -383,8 +383,10 @@ oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *
  * thread-safe: use it from one thread. */
 typedef struct oes_cpu_moe oes_cpu_moe;
 
-/* Create an executor for `schema` with `threads` worker threads (0: one per
- * CPU of the process's affinity mask; the calling thread is one of them).
+/* Create an executor for `schema` with `threads` worker threads (0: three
+ * quarters of the CPUs the process may use - its affinity mask capped by a
+ * cgroup CPU quota - which leaves room for the caller's other threads; the
+ * calling thread is one of the workers).
  * Errors: OES_ERR_ARG (schema not from oes_schema_make, threads outside
  * [0, 1024]), OES_ERR_UNSUPPORTED (a format without a CPU path, or a host
  * without AVX-512 F/BW/VL/BF16 and F16C). */
@@ -394,7 +396,9 @@ oes_status oes_cpu_moe_threads(const oes_cpu_moe *m, int32_t *threads);
 
 /* Register bank `bank` of layer `layer`: E rows of row_bytes, expert-major,
  * the same host tensors a cache reads (any host memory; caller-owned, must
- * outlive the executor).  bytes must equal E * row_bytes.  Errors: OES_ERR_ARG. */
+ * outlive the executor).  bytes must equal E * row_bytes.  Reads one byte of
+ * every 4 KiB page (on the executor's threads), so that the first-touch
+ * mapping of pinned pages happens here and not in a step.  Errors: OES_ERR_ARG. */
 oes_status oes_cpu_moe_set_source(oes_cpu_moe *m, int32_t bank, int32_t layer, const void *host, int64_t bytes);
 
 /* The CPU part of a hybrid step: for every pair (t, j) with slot_ids[t, j] < 0,
