@@ -20,7 +20,7 @@ Also printed (same JSON line): the copy sweep of the benchmark guide's columns
 25 event-timed ensure+copy repeats, fused and per-bank), decode tok/s at every
 miss rate, the measured ceilings (pinned H2D by DMA and by the zero-copy
 kernel, HBM streaming read, bf16 MFMA loop), the roofline of the dominant kernel and of the
-FFN, the hybrid backend (host DRAM read and link ceilings, the CPU MoE
+FFN, copy_missing of every decode bank format (8 misses), the hybrid backend (host DRAM read and link ceilings, the CPU MoE
 executor and the PCIe gather alone and overlapped, the decision and fetch
 split, the hybrid decode layer step beside the offload one), the cold decode
 FFN of every decode bank format (bf16, fp8 block, nvfp4,
@@ -234,6 +234,7 @@ def main():
     log("ffn", {"launches": n_ffn, "slot_maps": nsets, "ms_per_launch": round(ffn_alone_ms, 5)})
 
     ffn_formats = _ffn_formats(WORKLOADS, nsets, n_ffn, probes, log)
+    copy_formats = _copy_formats(WORKLOADS, probes, log)
 
     # ---------------------------------------------------------------- copy sweep
     sweep = []
@@ -333,7 +334,7 @@ def main():
                    "misses": head["misses"], "active": active, "bytes_per_expert": bpe},
         "tok_ms": head["tok_ms"], "copy_GBps": head.get("copy_GBps"),
         "roofline": roof, "kernels": kernels, "probes": probes, "decode_per_miss_rate": per_mr,
-        "copy_sweep": sweep, "ffn_formats": ffn_formats, "hybrid": hybrid, "resize": resize, "prefill": prefill,
+        "copy_sweep": sweep, "ffn_formats": ffn_formats, "copy_formats": copy_formats, "hybrid": hybrid, "resize": resize, "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -491,6 +492,61 @@ def _resize(cache, w, bpe, log):
            "grow_ms": (t2 - t1) * 1e3, "shrink_GBps": moved / ((t1 - t0) * 1e9),
            "grow_GBps": moved / ((t2 - t1) * 1e9)}
     log("resize", {k: (round(v, 3) if isinstance(v, float) else v) for k, v in out.items()})
+    return out
+
+
+def _copy_formats(workloads, probes, log, misses=8, repeats=10):
+    """copy_missing of every decode bank format at its workload's shape: `misses`
+    experts of layer 0 missing from a pool whose slots all belong to other layers
+    (benchmark guide §4.3), median of `repeats` (table restored before each, untimed).
+    The banks hold 2 * misses experts: the copy of a row does not depend on E."""
+    import numpy as np
+    import torch
+
+    import offloaded_expert_slot_amd as oes
+    import synth
+    from synth.workloads import Workload, make_host_banks
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("bf16_h2048", "fp8_h4096", "nvfp4_h7168", "q4_0_h2048"):
+        w0 = workloads[name]
+        E = 2 * misses
+        w = Workload(w0.name, w0.fmt, L=w0.L, E=E, k=misses, H=w0.H, I=w0.I, S=E)
+        hb = make_host_banks(w)
+        sc = oes.schema_make(w.fmt, w.L, E, w.H, w.I)
+        c = oes.Cache(sc, E, 0)
+        for b, t in enumerate(hb.banks):
+            c.set_source(b, 0, t)
+        owner, stamp, clock = synth.foreign_state(E, E)
+        c.set_state(owner, stamp, clock)
+        c.snapshot()
+        ids = torch.arange(misses, dtype=torch.int32, device=dev).reshape(1, misses)
+        slots = torch.empty_like(ids)
+        marks = []
+        for i in range(repeats + 2):
+            c.restore()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c.ensure_experts(0, ids, slots)
+            a.record(stream)
+            c.copy_missing()
+            b.record(stream)
+            if i >= 2:
+                marks.append((a, b))
+        torch.cuda.synchronize()
+        c.check()
+        ms = float(np.median([a.elapsed_time(b) for a, b in marks]))
+        nbytes = misses * sc.bytes_per_expert
+        row = {"format": w.fmt, "bytes_per_expert": sc.bytes_per_expert, "misses": misses, "copy_ms": ms,
+               "GBps": nbytes / (ms * 1e6)}
+        if probes:
+            row["frac_of_measured_h2d_peak"] = row["GBps"] / probes["h2d_peak_GBps"]
+        out[name] = row
+        log("copy format", {k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()})
+        c.close()
+        del hb
+    torch.cuda.empty_cache()
     return out
 
 
