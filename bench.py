@@ -279,6 +279,7 @@ def main():
     hybrid = None
     if not args.no_hybrid:
         hybrid = _hybrid(cache, hb, w, bpe, x, wg, rws, fws, prepare, probes, per_mr, args, log)
+        hybrid["formats"] = _cpu_formats(WORKLOADS, copy_formats, log)
 
     # ---------------------------------------------------------------- slot-pool resize
     resize = _resize(cache, w, bpe, log)
@@ -470,6 +471,57 @@ def _hybrid(cache, hb, w, bpe, x, wg, rws, fws, prepare, probes, per_mr, args, l
                 "hybrid_speedup": res["offload"]["ms_per_step"] / res["hybrid"]["ms_per_step"]})
     log("hybrid", {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in out.items() if kk != "step"}, res)
     cpu.close()
+    return out
+
+
+def _cpu_formats(workloads, copy_formats, log, experts=8, repeats=12):
+    """ft bench bw per format (benchmark guide §5.2): the CPU executor on `experts`
+    experts of one token (banks of 2 * experts experts, rotating over the two
+    halves) against that format's measured PCIe gather; the decision and the
+    fetch fraction.  Block fp8 has no CPU path and stays offload."""
+    import numpy as np
+
+    import offloaded_expert_slot_amd as oes
+    import synth
+    from synth.workloads import Workload, make_host_banks
+
+    out = {}
+    for name in ("bf16_h2048", "nvfp4_h7168", "q4_0_h2048", "fp8_h4096"):
+        w0 = workloads[name]
+        pcie = copy_formats[name]["GBps"]
+        row = {"format": w0.fmt, "pcie_gather_GBps": pcie}
+        if w0.fmt == "fp8_block128":
+            use, frac = oes.hybrid_decide(w0.fmt, 0.0, pcie)
+            row.update(cpu_moe_GBps=None, decision="hybrid" if use else "offload", fetch_fraction=frac)
+            out[name] = row
+            continue
+        E = 2 * experts
+        w = Workload(w0.name, w0.fmt, L=1, E=E, k=experts, H=w0.H, I=w0.I, S=E)
+        hb = make_host_banks(w)
+        sc = oes.schema_make(w.fmt, 1, E, w.H, w.I)
+        cpu = oes.CpuMoe(sc, 0)
+        for b, t in enumerate(hb.banks):
+            cpu.set_source(b, 0, t)
+        xh = synth.activations(1, w.H, 0, w.name)
+        sets = [np.arange(h * experts, (h + 1) * experts, dtype=np.int32).reshape(1, experts) for h in range(2)]
+        allcpu = np.full((1, experts), -1, dtype=np.int32)
+        wk = np.full((1, experts), 1.0 / experts, dtype=np.float32)
+        yc = np.zeros((1, w.H), dtype=np.float32)
+        for i in range(2):
+            cpu.run(0, xh, sets[i], allcpu, wk, yc)
+        ts = []
+        for i in range(repeats):
+            t0 = time.perf_counter()
+            cpu.run(0, xh, sets[i % 2], allcpu, wk, yc)
+            ts.append(time.perf_counter() - t0)
+        ms = float(np.median(ts)) * 1e3
+        gbps = experts * sc.bytes_per_expert / (ms * 1e6)
+        use, frac = oes.hybrid_decide(w.fmt, gbps, pcie)
+        row.update(cpu_moe_ms=ms, cpu_moe_GBps=gbps, decision="hybrid" if use else "offload", fetch_fraction=frac)
+        out[name] = row
+        log("cpu format", {k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()})
+        cpu.close()
+        del hb
     return out
 
 
