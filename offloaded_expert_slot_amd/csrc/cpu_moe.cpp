@@ -15,8 +15,8 @@
 //   pass 2: y[t][r] = sum_j w[t, j] * (Wd_e[r] . h_tj) over the CPU pairs in
 //           (t, j) order; output rows are cut into one range per thread.
 // The summation order depends on neither the thread count nor the timing.
-// Weights are read from the host banks 32 elements at a time and turned into
-// bf16 exactly (bf16 as is; e2m1 and q - 8 through a 32-entry table with
+// Weights are read from the host banks 32 or 64 elements at a time and turned
+// into bf16 exactly (bf16 as is; e2m1 and q - 8 through a 32-entry table with
 // vpermw), multiplied with the bf16 operand by vdpbf16ps (fp32 accumulate),
 // scaled per block (nvfp4: e4m3 per 16, then the fp16 row global; q4_0: fp16
 // per 32).  Needs AVX-512 F/BW/VL/BF16 and F16C; without them the executor is
@@ -222,6 +222,51 @@ OES_AVX512 float dot_nvfp4(const uint8_t *c, const uint8_t *sc, const uint16_t *
   return _mm512_reduce_add_ps(acc);
 }
 
+// up to 16 e4m3 bytes (mask mk) -> 16 floats (OCP e4m3: bias 7, subnormals
+// m * 2^-9, S.1111.111 NaN); masked-off bytes read as 0
+OES_AVX512 __m512 e4m3x16(const uint8_t *b, __mmask16 mk) {
+  const __m512i d = _mm512_cvtepu8_epi32(_mm_maskz_loadu_epi8(mk, b));
+  const __m512i sign = _mm512_slli_epi32(_mm512_and_si512(d, _mm512_set1_epi32(0x80)), 24);
+  const __m512i e = _mm512_and_si512(_mm512_srli_epi32(d, 3), _mm512_set1_epi32(15));
+  const __m512i m = _mm512_and_si512(d, _mm512_set1_epi32(7));
+  const __m512i normal = _mm512_or_si512(_mm512_slli_epi32(_mm512_add_epi32(e, _mm512_set1_epi32(120)), 23),
+                                         _mm512_slli_epi32(m, 20));
+  const __m512i sub = _mm512_castps_si512(_mm512_mul_ps(_mm512_cvtepi32_ps(m), _mm512_set1_ps(1.f / 512.f)));
+  __m512i mag = _mm512_mask_blend_epi32(_mm512_cmpeq_epi32_mask(e, _mm512_setzero_si512()), normal, sub);
+  mag = _mm512_mask_blend_epi32(_mm512_cmpeq_epi32_mask(_mm512_and_si512(d, _mm512_set1_epi32(0x7f)),
+                                                        _mm512_set1_epi32(0x7f)),
+                                mag, _mm512_set1_epi32(0x7fc00000));
+  return _mm512_castsi512_ps(_mm512_or_si512(mag, sign));
+}
+
+// nvfp4 row (K % 64 == 0) against the operand split into even (xe) and odd (xo)
+// elements, 64 elements per step: the 32 code bytes widen to 32 words whose low
+// nibbles are the even elements and high nibbles the odd ones, so two table
+// lookups and two chained vdpbf16ps cover the step; output lane i sums elements
+// 4i..4i+3 of the step, scale block 4 * step + i / 4.
+OES_AVX512 float dot_nvfp4_eo(const uint8_t *c, const uint8_t *sc, const uint16_t *xe, const uint16_t *xo, int K,
+                              const Tables &t) {
+  const __m512i lut = _mm512_load_si512(t.e2m1);
+  const __m512i nib = _mm512_set1_epi16(0xf);
+  const __m512i rep0 = _mm512_setr_epi32(0, 0, 0, 0, 1, 1, 1, 1, 2, 2, 2, 2, 3, 3, 3, 3);
+  __m512 acc = _mm512_setzero_ps();
+  __m512 s16 = _mm512_setzero_ps();
+  for (int g = 0; g < K / 64; ++g) {
+    if ((g & 3) == 0) {  // the scales of this step and the next three (masked at the row's end)
+      const int avail = K / 16 - 4 * g;
+      s16 = e4m3x16(sc + 4 * g, avail >= 16 ? (__mmask16)0xffff : (__mmask16)((1u << avail) - 1u));
+    }
+    const __m512i w = _mm512_cvtepu8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i *>(c + 32 * g)));
+    const __m512i lo = _mm512_and_si512(w, nib);
+    const __m512i hi = _mm512_srli_epi16(w, 4);
+    __m512 p = dp(_mm512_setzero_ps(), _mm512_permutexvar_epi16(lo, lut), _mm512_loadu_si512(xe + 32 * g));
+    p = dp(p, _mm512_permutexvar_epi16(hi, lut), _mm512_loadu_si512(xo + 32 * g));
+    const __m512i idx = _mm512_add_epi32(rep0, _mm512_set1_epi32(4 * (g & 3)));
+    acc = _mm512_fmadd_ps(p, _mm512_permutexvar_ps(idx, s16), acc);
+  }
+  return _mm512_reduce_add_ps(acc);
+}
+
 // GGUF Q4_0 row: 16 code bytes per 32-element block (byte j: element j low
 // nibble, element j + 16 high nibble), fp16 d per block.  K % 32 == 0.
 OES_AVX512 float dot_q4_0(const uint8_t *c, const uint16_t *d, const uint16_t *x, int K, const Tables &t) {
@@ -302,7 +347,8 @@ struct oes_cpu_moe {
   std::vector<const uint8_t *> src;  // [bank * L + layer]
   std::unique_ptr<Pool> pool;
   Tables tab;
-  std::vector<uint16_t> h;           // [pairs, I] bf16
+  std::vector<uint16_t> h;           // [pairs, I] bf16 (nvfp4: even elements, then odd)
+  std::vector<uint16_t> xeo;         // nvfp4: x split into even and odd elements
   std::vector<int32_t> pt, pj;       // CPU pairs in (t, j) order
 };
 
@@ -345,11 +391,14 @@ MatView mat_view(const oes_cpu_moe *m, int layer, int e, bool down) {
   return v;
 }
 
-OES_AVX512 float row_dot(int fmt, const MatView &v, int r, const uint16_t *x, const Tables &t) {
+// x: the operand in element order, or for nvfp4 with eo set its even elements
+// followed by its odd ones (K % 64 == 0)
+OES_AVX512 float row_dot(int fmt, const MatView &v, int r, const uint16_t *x, const Tables &t, bool eo) {
   const uint8_t *c = v.codes + (int64_t)r * v.row_bytes;
   if (fmt == OES_BF16) return dot_bf16(reinterpret_cast<const uint16_t *>(c), x, v.K);
   if (fmt == OES_NVFP4) {
-    const float s = dot_nvfp4(c, v.scale + (int64_t)r * v.scale_ld, x, v.K, t);
+    const uint8_t *sc = v.scale + (int64_t)r * v.scale_ld;
+    const float s = eo ? dot_nvfp4_eo(c, sc, x, x + v.K / 2, v.K, t) : dot_nvfp4(c, sc, x, v.K, t);
     return s * fp16_value(reinterpret_cast<const uint16_t *>(v.glob)[r]);
   }
   return dot_q4_0(c, reinterpret_cast<const uint16_t *>(v.scale + (int64_t)r * v.scale_ld), x, v.K, t);
@@ -451,6 +500,18 @@ extern "C" oes_status oes_cpu_moe_run(oes_cpu_moe *m, int32_t layer, const void 
   m->h.resize((size_t)P * I);
   const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
   const int fmt = sc.format;
+  // nvfp4 rows of a multiple of 64 elements take their operand as even elements
+  // then odd ones: x is split here, h is written split by pass 1
+  const bool eo_gu = fmt == OES_NVFP4 && H % 64 == 0, eo_dn = fmt == OES_NVFP4 && I % 64 == 0;
+  if (P && eo_gu) {
+    m->xeo.resize((size_t)n * H);
+    for (int t = 0; t < n; ++t)
+      for (int j = 0; j < H / 2; ++j) {
+        m->xeo[(size_t)t * H + j] = x[(int64_t)t * H + 2 * j];
+        m->xeo[(size_t)t * H + H / 2 + j] = x[(int64_t)t * H + 2 * j + 1];
+      }
+    x = m->xeo.data();
+  }
   const Tables &tab = m->tab;
   uint16_t *hb = m->h.data();
   const int32_t *pt = m->pt.data(), *pj = m->pj.data();
@@ -469,9 +530,10 @@ extern "C" oes_status oes_cpu_moe_run(oes_cpu_moe *m, int32_t layer, const void 
           cur = p;
         }
         const uint16_t *xt = x + (int64_t)pt[p] * H;
-        const float g = row_dot(fmt, v, r, xt, tab);
-        const float u = row_dot(fmt, v, r + I, xt, tab);
-        hb[it] = bf16_rne(g / (1.f + expf(-g)) * u);
+        const float g = row_dot(fmt, v, r, xt, tab, eo_gu);
+        const float u = row_dot(fmt, v, r + I, xt, tab, eo_gu);
+        const int64_t at = (int64_t)p * I + (eo_dn ? (r & 1) * (I / 2) + (r >> 1) : r);
+        hb[at] = bf16_rne(g / (1.f + expf(-g)) * u);
       }
     });
   }
@@ -485,7 +547,7 @@ extern "C" oes_status oes_cpu_moe_run(oes_cpu_moe *m, int32_t layer, const void 
       const float wt = w[pt[p] * k + pj[p]];
       float *yt = y + (int64_t)pt[p] * H;
       const uint16_t *hp = hb + (int64_t)p * I;
-      for (int r = lo; r < hi; ++r) yt[r] += wt * row_dot(fmt, v, r, hp, tab);
+      for (int r = lo; r < hi; ++r) yt[r] += wt * row_dot(fmt, v, r, hp, tab, eo_dn);
     }
   });
   return OES_OK;

@@ -42,6 +42,9 @@ def _rows(hb):
     ("bf16", 256, 128, 8, 3, 4), ("nvfp4", 512, 256, 8, 3, 4), ("q4_0", 512, 256, 8, 3, 4),
     ("bf16", 2048, 768, 16, 1, 8), ("q4_0", 2048, 768, 16, 4, 8), ("nvfp4", 7168, 2048, 6, 2, 4),
     ("bf16", 264, 136, 5, 2, 3),   # K not a multiple of 32: the masked tail
+    ("nvfp4", 288, 160, 6, 2, 3),  # rows not a multiple of 64: element-order nvfp4 path
+    ("nvfp4", 512, 160, 6, 2, 3),  # even/odd path for gate_up, element order for down
+    ("nvfp4", 4160, 192, 5, 1, 4), # 65 64-element steps: scales masked at the row's end
 ])
 def test_cpu_moe_matches_oracle(fmt, H, I, E, n, k):
     _case(f"cpu moe {fmt} H={H} I={I} n={n} k={k}")
