@@ -315,7 +315,7 @@ def main():
         kernels["prefill_ffn"] = {"bound": "mfma", "achieved": prefill["ffn_TFLOPs"], "peak": BF16_MFMA_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": prefill["ffn_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS,
                                   "flops_per_launch": prefill["flops"], "avg_ms": prefill["ffn_ms"],
-                                  "hbm_GBps": prefill["ffn_weight_GBps"], "traffic": None}
+                                  "hbm_GBps": prefill["ffn_weight_GBps"], "traffic": _pmc_traffic("prefill_ffn")}
         if probes:
             kernels["prefill_ffn"]["frac_of_measured_mfma_peak"] = prefill["ffn_TFLOPs"] / probes["mfma_bf16_TFLOPs"]
 
