@@ -80,8 +80,8 @@ int32_t oes_abi_version(void);
  *                     bytes, byte j holds element j in its low nibble and
  *                     element j+16 in its high nibble), gate_up_d [2I,H/32] fp16,
  *                     down_q [H,I/2], down_d [H,I/32] (W = (q - 8) * d of its
- *                     32-block; the fifth format of FreeToken architecture walk-through §5,
- *                     GGUF Q4_0 MoE in §6)
+ *                     32-block; the fifth format of FreeToken architecture
+ *                     walk-through §5, GGUF Q4_0 MoE in §6)
  */
 enum { OES_BF16 = 0, OES_FP8_BLOCK128 = 1, OES_NVFP4 = 2, OES_MXFP4_T = 3, OES_Q4_0 = 4 };
 enum {
@@ -108,8 +108,8 @@ typedef struct {
 
 /* Fill *out with the bank list of a format (the pages' bank_specs()).
  * Errors: OES_ERR_ARG for L, E, H, I <= 0, E > OES_MAX_EXPERTS, sizes the
- * format cannot tile (bf16: H, I multiples of 8; fp8: of 128; nvfp4: of 32;
- * mxfp4: of 32), or an unknown format.  Pure host code, no GPU needed. */
+ * format cannot tile (bf16: H, I multiples of 8; fp8: of 128; nvfp4, mxfp4
+ * and q4_0: of 32), or an unknown format.  Pure host code, no GPU needed. */
 oes_status oes_schema_make(int32_t format, int32_t num_layers, int32_t num_experts,
                            int32_t hidden, int32_t inter, oes_schema *out);
 
@@ -241,7 +241,8 @@ oes_status oes_route_workspace(int32_t n, int32_t hidden, int32_t num_experts, i
 
 /* Top-k routing: logits = x . Wg (bf16 inputs, fp32 sums), softmax over the E
  * experts, the k largest in descending order (equal logits: lower expert
- * first), weights renormalised to sum to 1 (the top-k of each MoE layer;
+ * first; a NaN logit ranks below every number), weights renormalised to sum
+ * to 1 (the top-k of each MoE layer;
  * benchmark guide §4.3 routes bs * topk experts per step).
  *   x   [n, H] bf16 device, wg [H, E] bf16 device (row-major)
  *   ids [n, k] int32 device out, w [n, k] float device out
@@ -311,8 +312,8 @@ oes_status oes_expert_ffn_workspace(const oes_cache *c, int32_t n, int32_t k, in
  *   x [n, H] bf16 device, slot_ids [n, k] int32 device (-1 = skip the pair),
  *   w [n, k] float device, y [n, H] bf16 device out, workspace device.
  * Formats: OES_BF16, OES_FP8_BLOCK128, OES_NVFP4, OES_Q4_0 (decode).  Limits:
- * n * k <= 65536, k <= 32.  A no-op when the last ensure_experts failed on the
- * device.  Async. */
+ * n * k <= 32768, k <= 32, H <= 16384.  A no-op when the last ensure_experts
+ * failed on the device.  Async. */
 oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
                           int32_t n, int32_t k, void *y, void *workspace, int64_t workspace_bytes,
                           void *stream);
