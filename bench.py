@@ -316,6 +316,10 @@ def main():
                                   "unit": "TFLOP/s", "frac": prefill["ffn_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS,
                                   "flops_per_launch": prefill["flops"], "avg_ms": prefill["ffn_ms"],
                                   "hbm_GBps": prefill["ffn_weight_GBps"], "traffic": _pmc_traffic("prefill_ffn")}
+        # the min(MFMA, HBM x intensity) roofline: 407.7 GFLOP over 1.694 GB of weights
+        ridge = min(BF16_MFMA_PEAK_TFLOPS, HBM_PEAK_GBS * prefill["flops"] / prefill["layer_bytes"] / 1e3)
+        kernels["prefill_ffn"]["min_roofline_TFLOPs"] = ridge
+        kernels["prefill_ffn"]["frac_of_min_roofline"] = prefill["ffn_TFLOPs"] / ridge
         if probes:
             kernels["prefill_ffn"]["frac_of_measured_mfma_peak"] = prefill["ffn_TFLOPs"] / probes["mfma_bf16_TFLOPs"]
 
