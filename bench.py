@@ -215,7 +215,7 @@ def main():
     # token where every layer has other experts.  Slot contents do not matter for
     # the time; the step loop above keeps its own state.
     rng = np.random.default_rng(0)
-    nsets = 16
+    nsets = max(1, min(16, w.S // w.k))   # disjoint slot maps the pool holds (16 for the bench workload)
     pool = rng.permutation(w.S)[: nsets * w.k]
     maps = [torch.from_numpy(pool[i * w.k:(i + 1) * w.k].astype(np.int32).reshape(1, w.k)).to(dev)
             for i in range(nsets)]
@@ -233,7 +233,7 @@ def main():
     ffn_bytes = w.k * bpe
     log("ffn", {"launches": n_ffn, "slot_maps": nsets, "ms_per_launch": round(ffn_alone_ms, 5)})
 
-    ffn_formats = _ffn_formats(WORKLOADS, nsets, n_ffn, probes, log)
+    ffn_formats = _ffn_formats(WORKLOADS, 16, n_ffn, probes, log)
     copy_formats = _copy_formats(WORKLOADS, probes, log)
 
     # ---------------------------------------------------------------- copy sweep
