@@ -216,15 +216,19 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
   // B: one quad's two pairs; pair p of quad q + 1 is loaded as soon as quad q's
   // steps on pair p are issued
   u32x4 bw[2][NTW];
-  const uint8_t *bptr[NTW];
-#pragma unroll
-  for (int t = 0; t < NTW; ++t) bptr[t] = blk + (int64_t)T.nrow[t] * 16;
   const int64_t kstride = (int64_t)T.N * 16;
+  uint32_t boff[NTW], soff[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    boff[t] = (uint32_t)(T.nrow[t] * 16 + h * T.N * 16);
+    soff[t] = (uint32_t)(h * kRowsB + T.lrow[t]);
+  }
+  auto pair_kb0 = [&](int p, int q) { return min(4 * q + 2 * p, T.nkb - 2); };
   auto load_bp = [&](int p, int q) {
-    const int kb = min(4 * q + 2 * p + h, T.nkb - 1);
+    const uint8_t *ub = blk + (int64_t)pair_kb0(p, q) * kstride;
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
-      bw[p][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(bptr[t] + kb * kstride));
+      bw[p][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ub + boff[t]));
   };
 
   auto quad = [&](int q, bool more) {
@@ -232,10 +236,10 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
     const uint16_t *Ab = As[q & 1];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int kb = min(4 * q + 2 * p + h, T.nkb - 1);
+      const uint8_t *sl = sc_lds + pair_kb0(p, q) * kRowsB;
       float sc[NTW];
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) sc[t] = e8m0_bits(sc_lds[kb * kRowsB + T.lrow[t]]);
+      for (int t = 0; t < NTW; ++t) sc[t] = e8m0_bits(sl[soff[t]]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8 bop[NTW];
@@ -359,17 +363,27 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
   }
   // scale bytes of the block's 256 weight rows: sc_lds[kb][local row], taken as
   // dwords of four rows (rows past the matrix clamp to its last dword; their
-  // tiles are never stored)
+  // tiles are never stored).  Thread (w, c) copies dword c of blocks w, w + 4,
+  // ..., w + 92: every load is issued before the first LDS write, so the staging
+  // costs one memory round trip instead of one per dword.  Blocks past K / 32
+  // get copies of the last block (the array holds kMaxKb of them; the quad loop
+  // clamps its block index below K / 32, so they are never read).
   {
-    const uint8_t *scl = g.scales + (int64_t)T.e * g.scales_stride;
-    for (int i = threadIdx.x; i < T.nkb * (kRowsB / 4); i += kThreads) {
-      const int kb = i / (kRowsB / 4), r4 = (i % (kRowsB / 4)) * 4;
-      int row;
-      if (PHASE == 0) row = r4 < 128 ? min(nt * 128 + r4, g.I - 4) : g.I + min(nt * 128 + r4 - 128, g.I - 4);
-      else row = min(nt * 256 + r4, T.N - 4);
-      *reinterpret_cast<uint32_t *>(&sc_lds[kb * kRowsB + r4]) =
-          *reinterpret_cast<const uint32_t *>(scl + (int64_t)kb * T.N + row);
+    constexpr int kScPer = kMaxKb * (kRowsB / 4) / kThreads;  // dwords per thread at most
+    static_assert(kRowsB / 4 == 64 && kThreads == 256, "a wave copies one scale block row per step");
+    const int r4 = lane * 4;
+    int row;
+    if (PHASE == 0) row = r4 < 128 ? min(nt * 128 + r4, g.I - 4) : g.I + min(nt * 128 + r4 - 128, g.I - 4);
+    else row = min(nt * 256 + r4, T.N - 4);
+    const uint8_t *scl = g.scales + (int64_t)T.e * g.scales_stride + row;
+    uint32_t sv[kScPer];
+#pragma unroll
+    for (int u = 0; u < kScPer; ++u) {
+      const int kb = min(wave + 4 * u, T.nkb - 1);
+      sv[u] = *reinterpret_cast<const uint32_t *>(scl + (int64_t)kb * T.N);
     }
+#pragma unroll
+    for (int u = 0; u < kScPer; ++u) *reinterpret_cast<uint32_t *>(&sc_lds[(wave + 4 * u) * kRowsB + r4]) = sv[u];
   }
   const int lda_src = PHASE == 0 ? g.H : g.I;
 
