@@ -117,9 +117,9 @@ hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t s);
 int64_t mfma_probe_flops(int blocks, int iters);
 
 // ---------------------------------------------------------------- debug decode
-// out[i] = value of element i of `elem` codes (fp4x2: 2 per byte, element 2j low nibble)
 // y[i] = bf16_rne(float(y[i]) + add[i]) for i < count (device buffers)
 hipError_t launch_add_to_bf16(uint16_t *y, const float *add, int64_t count, hipStream_t s);
+// out[i] = value of element i of `elem` codes (fp4x2: 2 per byte, element 2j low nibble)
 hipError_t launch_debug_decode(int elem, const uint8_t *codes, int n, float *out, hipStream_t s);
 
 }  // namespace oes
