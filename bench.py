@@ -107,6 +107,7 @@ def main():
         sink = torch.zeros(4, dtype=torch.float32, device=dev)
         hbm = [oes.probe_hbm_read(big, big.numel(), sink) for _ in range(5)]
         mfma = [oes.probe_mfma_bf16(2048, 10000, sink) for _ in range(3)]
+        mfma_f8f4 = [oes.probe_mfma_f8f4(2048, 5000, sink) for _ in range(3)]
         # streaming reads of the FFN's byte count, back to back over 16 distinct
         # regions (1.2 GB), timed like the FFN alone below
         fb = (w.k * bpe // 16) * 16
@@ -117,6 +118,7 @@ def main():
             "h2d_zero_copy_GBps": nbytes / (min(zc) * 1e6),
             "hbm_read_GBps": big.numel() / (min(hbm) * 1e6),
             "mfma_bf16_TFLOPs": max(fl / (ms * 1e9) for ms, fl in mfma),
+            "mfma_f8f4_TFLOPs": max(fl / (ms * 1e9) for ms, fl in mfma_f8f4),
             "hbm_read_ffn_bytes_GBps": fb / (min(hbm_small) * 1e6),
             "ffn_bytes": fb,
             "h2d_bytes": nbytes,
@@ -320,8 +322,13 @@ def main():
         ridge = min(BF16_MFMA_PEAK_TFLOPS, HBM_PEAK_GBS * prefill["flops"] / prefill["layer_bytes"] / 1e3)
         kernels["prefill_ffn"]["min_roofline_TFLOPs"] = ridge
         kernels["prefill_ffn"]["frac_of_min_roofline"] = prefill["ffn_TFLOPs"] / ridge
+        # each bf16 x fp4 product runs as two e4m3 x e2m1 block-scaled MFMAs (the
+        # activation's hi and lo planes), which issue at twice the bf16 rate: the
+        # measured ceiling of the product is half the f8f4 loop's issued rate
+        kernels["prefill_ffn"]["instruction"] = "v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e2m1), two per product"
         if probes:
-            kernels["prefill_ffn"]["frac_of_measured_mfma_peak"] = prefill["ffn_TFLOPs"] / probes["mfma_bf16_TFLOPs"]
+            kernels["prefill_ffn"]["measured_mfma_ceiling_TFLOPs"] = probes["mfma_f8f4_TFLOPs"] / 2.0
+            kernels["prefill_ffn"]["frac_of_measured_mfma_peak"] = prefill["ffn_TFLOPs"] / (probes["mfma_f8f4_TFLOPs"] / 2.0)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

@@ -361,16 +361,19 @@ oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x, const int
  *   caller's buffer spans (count - 1) * stride + bytes; bytes and stride are
  *   multiples of 16, count >= 1.
  * oes_probe_mfma_bf16: `blocks` workgroups of 4 waves, each wave `iters` rounds of
- *   4 independent v_mfma_f32_32x32x16_bf16 (the prefill GEMM's instruction) on
- *   register operands; `*flops` receives the dense flops issued.  `sink` is a
- *   device float the kernel may write (it never does in practice).  blocks >= 1,
- *   1 <= iters <= 1 << 24. */
+ *   4 independent v_mfma_f32_32x32x16_bf16 on register operands; `*flops`
+ *   receives the dense flops issued.  `sink` is a device float the kernel may
+ *   write (it never does in practice).  blocks >= 1, 1 <= iters <= 1 << 24.
+ * oes_probe_mfma_f8f4: the same with v_mfma_scale_f32_32x32x64_f8f6f4, A e4m3 and
+ *   B e2m1 with e8m0 block scales (the prefill GEMM's instruction). */
 oes_status oes_probe_h2d_dma(void *dev, const void *host, int64_t bytes, void *stream, float *ms);
 oes_status oes_probe_h2d_kernel(void *dev, const void *host, int64_t bytes, int32_t blocks,
                                 void *stream, float *ms);
 oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, int64_t stride, int32_t count, void *sink,
                               void *stream, float *ms);
 oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
+                               double *flops);
+oes_status oes_probe_mfma_f8f4(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
                                double *flops);
 
 /* ------------------------------------------------------------------ decoder check */

@@ -116,6 +116,7 @@ _SIGS = {
     "oes_probe_h2d_kernel": (_I32, [_P, _P, _I64, _I32, _P, _PF]),
     "oes_probe_hbm_read": (_I32, [_P, _I64, _I64, _I32, _P, _P, _PF]),
     "oes_probe_mfma_bf16": (_I32, [_I32, _I32, _P, _P, _PF, ctypes.POINTER(ctypes.c_double)]),
+    "oes_probe_mfma_f8f4": (_I32, [_I32, _I32, _P, _P, _PF, ctypes.POINTER(ctypes.c_double)]),
     "oes_debug_decode": (_I32, [_I32, _P, _I32, _P, _P]),
     "oes_cache_resize": (_I32, [_P, _I32, _P]),
     "oes_cpu_moe_create": (_I32, [ctypes.POINTER(Schema), _I32, ctypes.POINTER(_P)]),
@@ -491,4 +492,11 @@ def probe_mfma_bf16(blocks, iters, sink, stream=None):
     """(ms, flops) of the bf16 MFMA loop: blocks x 4 waves x iters x 4 chained 32x32x16 MFMAs."""
     ms, flops = ctypes.c_float(), ctypes.c_double()
     _check(lib().oes_probe_mfma_bf16(blocks, iters, _ptr(sink), _stream(stream), ctypes.byref(ms), ctypes.byref(flops)))
+    return ms.value, flops.value
+
+
+def probe_mfma_f8f4(blocks, iters, sink, stream=None):
+    """(ms, flops) of the block-scaled e4m3 x e2m1 MFMA loop (32x32x64), the prefill GEMM's instruction."""
+    ms, flops = ctypes.c_float(), ctypes.c_double()
+    _check(lib().oes_probe_mfma_f8f4(blocks, iters, _ptr(sink), _stream(stream), ctypes.byref(ms), ctypes.byref(flops)))
     return ms.value, flops.value

@@ -1222,8 +1222,8 @@ extern "C" oes_status oes_probe_hbm_read(const void *dev, int64_t bytes, int64_t
   return st;
 }
 
-extern "C" oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
-                                          double *flops) {
+static oes_status probe_mfma(bool f8f4, int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
+                             double *flops) {
   if (blocks < 1 || iters < 1 || iters > (1 << 24) || !sink || !ms || !flops)
     return fail(OES_ERR_ARG, "bad probe arguments");
   hipStream_t s = as_stream(stream);
@@ -1231,10 +1231,20 @@ extern "C" oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *s
   HIP_TRY(hipEventCreate(&e0));
   HIP_TRY(hipEventCreate(&e1));
   HIP_TRY(hipEventRecord(e0, s));
-  HIP_TRY(launch_mfma_probe(blocks, iters, static_cast<float *>(sink), s));
+  HIP_TRY(launch_mfma_probe(f8f4, blocks, iters, static_cast<float *>(sink), s));
   HIP_TRY(hipEventRecord(e1, s));
-  *flops = (double)mfma_probe_flops(blocks, iters);
+  *flops = (double)mfma_probe_flops(f8f4, blocks, iters);
   return timed(s, ms, e0, e1);
+}
+
+extern "C" oes_status oes_probe_mfma_bf16(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
+                                          double *flops) {
+  return probe_mfma(false, blocks, iters, sink, stream, ms, flops);
+}
+
+extern "C" oes_status oes_probe_mfma_f8f4(int32_t blocks, int32_t iters, void *sink, void *stream, float *ms,
+                                          double *flops) {
+  return probe_mfma(true, blocks, iters, sink, stream, ms, flops);
 }
 
 // ============================================================================ hybrid step

@@ -1,31 +1,49 @@
-// Prefill grouped expert FFN over a streamed layer buffer: MXFP4 weights, bf16 MFMA.
+// Prefill grouped expert FFN over a streamed layer buffer: MXFP4 weights on the
+// gfx950 block-scaled MFMA.
 //
 // FreeToken architecture walk-through §5: prefill streams whole layers through a
 // double buffer; the FFN of a layer runs on the buffer holding it (row e =
 // expert e).  FreeToken MoE benchmark guide §4.2: the MXFP4 format keeps six
 // transposed banks - _blocks, _scales, _bias for gate_up and for down.
 //
-// Four launches:
+// Five launches:
 //   permute    - one workgroup counts the (token, pair) routes per expert, scans
 //                the counts into offsets and scatters the pair indices into
 //                expert order (perm).  The order inside an expert does not
 //                change any result: every output row of a GEMM is computed on
 //                its own, with the same k order.
-//   gemm<0>    - per expert e: h = silu(X_e Wg_e^T + bg) * (X_e Wu_e^T + bu), bf16,
-//                X_e the gathered activation rows of the pairs routed to e.
+//   split      - the bf16 activations x become two e4m3 code planes, hi and lo,
+//                with one power-of-two scale per 32-element block (below).
+//   gemm<0>    - per expert e: h = silu(X_e Wg_e^T + bg) * (X_e Wu_e^T + bu),
+//                rounded to bf16 and split like x, X_e the gathered activation
+//                rows of the pairs routed to e.
 //   gemm<1>    - per expert e: o = h_e Wd_e^T + bd, fp32, scattered back to the
 //                pair's row.
 //   combine    - y_t = sum_j w[t, j] * o_{t,j} in pair order, bf16.
 //
-// GEMM tiling (v_mfma_f32_32x32x16_bf16, details at the kernel):
+// Exact two-plane activations.  The weights stay MXFP4 (e2m1 codes with an e8m0
+// scale per 32 k) and go to v_mfma_scale_f32_32x32x64_f8f6f4 as they are, with
+// no conversion.  The activations are bf16 (8 significant bits); the MFMA's
+// other operand takes e4m3 (4 significant bits) with an e8m0 scale per 32 k.
+// Each 32-element block of a bf16 row is written as v = hi * 2^s + lo * 2^(s-4):
+// s puts the block's largest magnitude in [2^7, 2^8), hi is v / 2^s rounded to
+// e4m3, and the remainder (v / 2^s - hi) * 16 has at most 4 significant bits
+// and lies below 2^8, so lo holds it exactly.  The split is exact for every
+// element within 2^13 of its block's largest (smaller ones keep an error below
+// 2^-20 of that largest), so the two MFMAs per product compute what a bf16 x
+// fp4 product computes, with fp32 accumulation.  On gfx950 the fp8 x fp4 form
+// issues at twice the bf16 MFMA's flop rate, so the pair costs no more than
+// one bf16 MFMA over the same k, and the weights need no fp4 -> bf16 step.
+//
+// GEMM tiling (details at the kernel):
 //   block = (expert, 128 / 256 output features) x all rows of the expert in
 //   passes of 96; in gate_up, wave w owns 32 features (those 32 gate rows and
 //   the matching 32 up rows, so silu(g) * u is formed in registers).  K runs in
-//   quads of four 32-element MXFP4 blocks.  The A chunk of a quad is staged in
-//   LDS from registers loaded one quad ahead; the B operand needs no LDS: the
-//   K-block-major layout [K/32][N][16 B] gives each lane one 16-byte load per
-//   pair of blocks that feeds four MFMAs after fp4 -> bf16 scaled conversions
-//   (exact: e2m1 * 2^k is a bf16 number).
+//   quads of four 32-element MXFP4 blocks, each quad in two 64-k MFMA steps.
+//   The A chunk of a quad (hi and lo codes and the row's four scale bytes) is
+//   staged in LDS from registers loaded one quad ahead; the B operand needs no
+//   LDS: the K-block-major layout [K/32][N][16 B] gives each lane the 16 bytes
+//   of one MXFP4 block, which is its whole operand of one MFMA step.
 //   Blocks are mapped XCD-aware: hardware deals consecutive block indices to
 //   the 8 XCDs in turn, so block b runs on XCD b % 8; experts e with e % 8 == x
 //   are given to XCD x, which keeps an expert's activation rows in one L2
@@ -42,26 +60,30 @@ namespace oes {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;  // a global-memory u32x4
 
 constexpr int kThreads = 256;
 constexpr int BM = 96;             // rows per pass: three 32-row m-tiles
-constexpr int LDA = 128 + 8;       // LDS row of one 128-k quad, bf16 elements, padded 16 B
+constexpr int LDA = 256 + 16;      // LDS bytes per A row of one quad: 128 hi codes, 128 lo codes, 16 pad
 constexpr int kXcds = 8;
-constexpr int kProbeChains = 4;    // accumulator chains per wave of the MFMA ceiling probe
+constexpr int kProbeChains = 4;    // accumulator chains per wave of the MFMA ceiling probes
 constexpr int kMaxKb = 96;         // K / 32 limit of the grouped GEMM (K <= 3072)
-static_assert(kThreads == 256, "two A pieces per thread cover one row of each half m-tile");
+constexpr int kLoShift = 4;        // lo plane scale = hi plane scale / 2^4
+constexpr int kFmtE4m3 = 0, kFmtE2m1 = 4;  // operand formats of the block-scaled MFMA
+static_assert(kThreads == 256, "sixteen A pieces per row: 16 rows per thread group pass");
 
 struct GemmArgs {
   int32_t H, I, E, k, nk;
   int32_t ntiles;        // feature tiles per expert
   int32_t xcd;           // 1: XCD-aware block mapping (E % 8 == 0)
-  const uint16_t *x;     // [n, H] bf16
+  const uint8_t *ahi;    // this phase's A: e4m3 hi codes [rows, K]
+  const uint8_t *alo;    // e4m3 lo codes [rows, K]
+  const uint8_t *asc;    // hi scale bytes [rows, kb4(K)] (lo scale = hi - 4)
   const int32_t *offsets;  // [E + 1]
   const int32_t *perm;     // [nk] pair indices in expert order
   const uint8_t *blocks;   // this phase's _blocks bank, expert stride blocks_stride
@@ -69,9 +91,13 @@ struct GemmArgs {
   const uint16_t *bias;    // this phase's _bias bank (bf16)
   int64_t blocks_stride, scales_stride, bias_stride;
   const u32x4 *zero16;   // 16 zero bytes: the source of A pieces past K
-  uint16_t *hbuf;        // [nk, I] bf16, expert order
+  uint8_t *hhi, *hlo;    // gate_up output h: e4m3 planes [nk, I], expert order
+  uint8_t *hsc;          // its hi scale bytes [nk, kb4(I)]
   float *obuf;           // [nk, H] fp32, pair order
 };
+
+// scale bytes per row of a split plane: K / 32 rounded up to whole quads of four
+__host__ __device__ inline int kb4_of(int K) { return ((K / 32) + 3) & ~3; }
 
 __device__ inline float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ inline uint16_t to_bf16(float f) {
@@ -80,20 +106,25 @@ __device__ inline uint16_t to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-// e8m0 byte -> fp32 scale 2^(e-127); 0 -> 2^-127 (subnormal), 255 -> NaN
-__device__ inline float e8m0f(uint32_t e) {
-  return e == 255u ? __uint_as_float(0x7fc00000u) : (e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23));
-}
-// eight e2m1 codes (low nibble first) times a power-of-two scale -> bf16x8 operand
-__device__ inline bf16x8 fp4x8_bf16(uint32_t v, float s) {
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3);
-  bf16x8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+
+// Two-plane split of one bf16 value v held by lane (c, half) of a 32-lane half
+// whose lanes hold the 32 elements of one block: every lane of the half must
+// call it together (the block's largest magnitude is reduced over the half).
+// hi / lo are e4m3 codes, sbyte the hi plane's e8m0 scale byte, kept in
+// [4, 250] so that the lo scale sbyte - 4 is a finite e8m0 value too.
+struct Split {
+  uint32_t hi, lo, sbyte;
+};
+__device__ __forceinline__ Split split_e4m3(float v) {
+  uint32_t a = __float_as_uint(v) & 0x7fffffffu;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+  const uint32_t sb = (uint32_t)min(max((int)(a >> 23) - 7, 4), 250);
+  const float xs = v * __uint_as_float((254u - sb) << 23);  // v / 2^(sb - 127), exact
+  const uint32_t hp = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xs, 0.f, 0, false);
+  const float hf = __builtin_amdgcn_cvt_f32_fp8((int)hp, 0);
+  const uint32_t lp = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((xs - hf) * 16.f, 0.f, 0, false);
+  return {hp & 0xffu, lp & 0xffu, sb};
 }
 
 // ------------------------------------------------------------------ permute
@@ -125,32 +156,83 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int n
   }
 }
 
+// ------------------------------------------------------------------ split
+// x [rows, K] bf16 -> hi / lo e4m3 planes [rows, K] and hi scale bytes
+// [rows, kb4(K)], the same two-plane split as split_e4m3 with eight elements
+// per lane: four lanes hold a 32-element block (K % 64 == 0, so blocks never
+// straddle rows and count = rows * K is a multiple of 32: each group of four
+// lanes is wholly in or out).  The scale bytes past K / 32 (up to the quad) get
+// 127 (scale 1): the GEMMs multiply them by zero codes only.
+__global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t *x, int64_t count, int K, uint8_t *hi,
+                                                         uint8_t *lo, uint8_t *sc) {
+  const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (i >= count) return;
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + i));
+  float f[8];
+  uint32_t a = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __uint_as_float(v[j] << 16);
+    f[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    a = max(a, max(__float_as_uint(f[2 * j]) & 0x7fffffffu, __float_as_uint(f[2 * j + 1]) & 0x7fffffffu));
+  }
+  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+  const uint32_t sb = (uint32_t)min(max((int)(a >> 23) - 7, 4), 250);
+  const float inv = __uint_as_float((254u - sb) << 23);
+  u32x2 hv, lv;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const float x0 = f[4 * w] * inv, x1 = f[4 * w + 1] * inv, x2 = f[4 * w + 2] * inv, x3 = f[4 * w + 3] * inv;
+    int hp = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    hp = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hp, true);
+    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hp, false);
+    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hp, true);
+    int lp = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - h01[0]) * 16.f, (x1 - h01[1]) * 16.f, 0, false);
+    lp = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - h23[0]) * 16.f, (x3 - h23[1]) * 16.f, lp, true);
+    hv[w] = (uint32_t)hp;
+    lv[w] = (uint32_t)lp;
+  }
+  *reinterpret_cast<u32x2 *>(hi + i) = hv;
+  *reinterpret_cast<u32x2 *>(lo + i) = lv;
+  const int64_t row = i / K;
+  const int col = (int)(i - row * K);
+  const int nkb = K / 32, kb4 = kb4_of(K);
+  if ((col & 31) == 0) sc[row * kb4 + col / 32] = (uint8_t)sb;
+  if (col == 0)
+    for (int j = nkb; j < kb4; ++j) sc[row * kb4 + j] = 127;
+}
+
 // ------------------------------------------------------------------ grouped GEMM
 // Block = (expert, feature tile), 4 waves; rows of the expert in passes of at
 // most BM = 96, each pass run by a body specialised on its count of 32-row
-// m-tiles so that its quad loop has no branches.  v_mfma_f32_32x32x16_bf16:
-// lane l holds A[l%32][8(l/32)..+7] and B[8(l/32)..+7][l%32]; D element r of
-// lane l is row 4(l/32) + (r%4) + 8(r/4), column l%32.
+// m-tiles so that its quad loop has no branches.
 //
-// K order.  K runs in quads of four 32-element MXFP4 blocks (128 k), a quad in
-// two pairs.  An MFMA sums over its 16 k-slots in any order as long as A and B
-// use the same one, so in step j (0..3) of the pair starting at block kb0, lane
-// half h = l/32 feeds k-slots 8h..8h+7 with the real k = 32(kb0 + h) + 8j + i.
-// Lane (n, h) then needs all 32 codes of block kb0 + h of weight row n: the 16
-// contiguous bytes at (kb0 + h, n) of the [K/32][N][16] bank, one 16-byte load
-// per lane for four MFMAs, with one scale byte.
+// v_mfma_scale_f32_32x32x64_f8f6f4, A e4m3 and B e2m1 (lane layout checked on
+// the GPU with an in-bounds probe): in lane l = (c, h) with c = l % 32 and
+// h = l / 32, B is column c, k = 32h + i for code i of the lane's 16 bytes
+// (low nibble first), with the lane's scale byte; A is row c, bytes 0..15 at
+// k = 16h + i and bytes 16..31 at k = 32 + 16h + i, and the scale byte of lane
+// (c, h) scales A's k-block h (k = 32h .. 32h + 31).  D element r of lane l is
+// row 4h + (r % 4) + 8(r / 4), column c.
 //
-// Pipelining.  The block's scale bytes (its 256 weight rows x K/32 blocks) are
-// copied to LDS once.  B: each wave holds one quad's two pairs per n-tile in
-// registers; pair p of quad q + 1 is loaded as soon as quad q's MFMA steps on
-// pair p are issued.  A: the chunk of quad q + 1 (the pass's rows x 128 k,
-// bf16) is loaded into registers while quad q is multiplied from LDS, then
-// stored to the other LDS buffer; one barrier per quad.  The steady-state loop
-// has no conditions, so the compiler's memory-counter waits stay exact.
-// Indexes past the data are clamped (B) or pointed at a zero block (A, k past
-// K), never branched on.  Each output row of an MFMA depends only on its own A
-// row, so A rows past the pass's last row may hold anything: their outputs are
-// never stored.
+// K order.  Step j (0, 1) of quad q covers MXFP4 blocks kb0 = 4q + 2j and
+// kb0 + 1: lane (n, h) of a weight tile loads the 16 bytes at (kb0 + h, n) of
+// the [K/32][N][16] bank, which is its whole B operand; lane (m, h) of the A
+// side reads its 2 x 16 bytes of each plane from the staged row.
+//
+// Pipelining.  The block's weight scale bytes (its 256 weight rows x K/32
+// blocks) are copied to LDS once.  B: each wave holds one quad's two steps per
+// n-tile in registers; step j of quad q + 1 is loaded as soon as quad q's MFMAs
+// of step j are issued.  A: the chunk of quad q + 1 (the pass's rows x 128 k of
+// both planes, and each row's four scale bytes) is loaded into registers while
+// quad q is multiplied from LDS, then stored to the other LDS buffer; one
+// barrier per quad.  The steady-state loop has no conditions, so the
+// compiler's memory-counter waits stay exact.  Indexes past the data are
+// clamped (B) or pointed at a zero block (A, k past K), never branched on; the
+// A scale bytes past K / 32 are finite, so those steps add exact zeros.  Each
+// output row of an MFMA depends only on its own A row, so A rows past the
+// pass's last row may hold anything: their outputs are never stored.
 //
 // Each wave owns two 32-feature n-tiles: gate_up - the gate tile and the up
 // tile of the same 32 features (128 features per block); down - two consecutive
@@ -162,26 +244,23 @@ constexpr int kRowsB = 256;  // weight rows per block
 
 struct Tile {
   int e, off, m0, mrows;
-  int K, N, nkb, nq;
+  int K, N, nkb, nq, kb4;
   int nrow[NTW], f[NTW], lrow[NTW];
   bool tile_on[NTW];
   int n32, h;
 };
 
-// e8m0 byte -> fp32 2^(e-127): e << 23, with 0 -> 2^-127 (0x00400000) and
-// 255 -> NaN (0x7fc00000), both by setting bit 22; no branches
-__device__ __forceinline__ float e8m0_bits(uint32_t e) {
-  return __uint_as_float((e << 23) | ((uint32_t)(e == 0u || e == 255u) << 22));
-}
-
 template <int PHASE, int MT>
-__device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint16_t (*As)[BM * LDA],
-                                          const int32_t *rowoff, const uint8_t *sc_lds) {
+__device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint8_t (*As)[BM * LDA],
+                                          uint32_t (*Asc)[kThreads], const int32_t *rowidx,
+                                          const uint8_t *sc_lds) {
   constexpr int AP = 2 * MT;  // 16-byte A pieces per thread per quad
   const uint8_t *blk = g.blocks + (int64_t)T.e * g.blocks_stride;
-  const uint16_t *asrc = PHASE == 0 ? g.x : g.hbuf;
   const int n32 = T.n32, h = T.h;
-  const int c16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;  // A piece: row 16i + rsub, column c16
+  // A piece: row 16i + rsub, 16 bytes at c16 * 16 of the staged row (hi plane for
+  // c16 < 8, lo plane for c16 >= 8)
+  const int c16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;
+  const uint8_t *psrc = (c16 < 8 ? g.ahi : g.alo) + (c16 & 7) * 16;
 
   f32x16 acc[MT][NTW];
 #pragma unroll
@@ -191,30 +270,39 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
 
-  // A rows: rowoff < 0 marks a row past the pass (read row 0 instead)
-  int32_t aoff[AP];
+  // A rows: rowidx < 0 marks a row past the pass (read row 0 instead)
+  uint32_t aoff[AP];
 #pragma unroll
-  for (int i = 0; i < AP; ++i) aoff[i] = max(rowoff[16 * i + rsub], 0);
+  for (int i = 0; i < AP; ++i) aoff[i] = (uint32_t)max(rowidx[16 * i + rsub], 0) * (uint32_t)T.K;
+  // thread t also stages the four scale bytes per quad of row min(t, BM - 1)
+  // (the m-tiles read those of rows below 32 * MT); no thread is left out, so
+  // the staging has no branch
+  const uint8_t *ssrc = g.asc + (uint32_t)max(rowidx[min((int)threadIdx.x, BM - 1)], 0) * (uint32_t)T.kb4;
   // pieces past K read the zero block: a select on the loaded value would make
   // the wave wait for the loads at once instead of at the quad's end
   const uint64_t zero_addr = reinterpret_cast<uint64_t>(g.zero16);
   u32x4 areg[AP];
+  uint32_t sreg;
   auto load_a = [&](int q) {
-    const int k0 = q * 128 + c16 * 8;
-    const bool kin = k0 < T.K;
+    const int k0 = q * 128;
+    const bool kin = k0 + (c16 & 7) * 16 < T.K;
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
-      uint64_t src = kin ? reinterpret_cast<uint64_t>(asrc + aoff[i] + k0) : zero_addr;
+      uint64_t src = kin ? reinterpret_cast<uint64_t>(psrc + aoff[i] + k0) : zero_addr;
       asm volatile("" : "+v"(src));  // keep the select on the address
-      areg[i] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4 *>(src));
+      // every feature-tile block of the expert reads these rows: keep them in L2
+      // (the weights, read once, are loaded non-temporal)
+      areg[i] = *reinterpret_cast<const gu32x4 *>(src);
     }
+    sreg = *reinterpret_cast<const uint32_t *>(ssrc + 4 * q);
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4 *>(&As[buf][(16 * i + rsub) * LDA + c16 * 8]) = areg[i];
+    for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4 *>(&As[buf][(16 * i + rsub) * LDA + c16 * 16]) = areg[i];
+    Asc[buf][threadIdx.x] = sreg;
   };
-  // B: one quad's two pairs; pair p of quad q + 1 is loaded as soon as quad q's
-  // steps on pair p are issued
+  // B: one quad's two steps; step j of quad q + 1 is loaded as soon as quad q's
+  // MFMAs of step j are issued
   u32x4 bw[2][NTW];
   const int64_t kstride = (int64_t)T.N * 16;
   uint32_t boff[NTW], soff[NTW];
@@ -223,45 +311,62 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
     boff[t] = (uint32_t)(T.nrow[t] * 16 + h * T.N * 16);
     soff[t] = (uint32_t)(h * kRowsB + T.lrow[t]);
   }
-  auto pair_kb0 = [&](int p, int q) { return min(4 * q + 2 * p, T.nkb - 2); };
-  auto load_bp = [&](int p, int q) {
-    const uint8_t *ub = blk + (int64_t)pair_kb0(p, q) * kstride;
+  auto step_kb0 = [&](int j, int q) { return min(4 * q + 2 * j, T.nkb - 2); };
+  auto load_b = [&](int j, int q) {
+    const uint8_t *ub = blk + (int64_t)step_kb0(j, q) * kstride;
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
-      bw[p][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ub + boff[t]));
+      bw[j][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ub + boff[t]));
   };
 
-  auto quad = [&](int q, bool more) {
-    if (more) load_a(q + 1);
-    const uint16_t *Ab = As[q & 1];
+  // one 64-k step: per m-tile, the hi plane's MFMAs on both n-tiles, then the lo plane's
+  auto step = [&](int j, int q, const uint8_t *Ab, const uint32_t *sdw) {
+    const uint8_t *sl = sc_lds + step_kb0(j, q) * kRowsB;
+    int sbv[NTW];
+    i32x8 bop[NTW];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint8_t *sl = sc_lds + pair_kb0(p, q) * kRowsB;
-      float sc[NTW];
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) sc[t] = e8m0_bits(sl[soff[t]]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 bop[NTW];
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) bop[t] = fp4x8_bf16(bw[p][t][j], sc[t]);
-        if (j == 3) load_bp(p, q + 1);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 av =
-              *reinterpret_cast<const bf16x8 *>(&Ab[(mt * 32 + n32) * LDA + (2 * p + h) * 32 + j * 8]);
-#pragma unroll
-          for (int t = 0; t < NTW; ++t)
-            acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bop[t], acc[mt][t], 0, 0, 0);
-        }
-      }
+    for (int t = 0; t < NTW; ++t) {
+      sbv[t] = sl[soff[t]];
+      bop[t] = i32x8{(int)bw[j][t][0], (int)bw[j][t][1], (int)bw[j][t][2], (int)bw[j][t][3], 0, 0, 0, 0};
     }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint8_t *ar = Ab + (mt * 32 + n32) * LDA + 64 * j + 16 * h;
+      const u32x4 h0 = *reinterpret_cast<const u32x4 *>(ar), h1 = *reinterpret_cast<const u32x4 *>(ar + 32);
+      const u32x4 l0 = *reinterpret_cast<const u32x4 *>(ar + 128), l1 = *reinterpret_cast<const u32x4 *>(ar + 160);
+      const int sah = (int)((sdw[mt] >> (8 * (2 * j + h))) & 0xffu);
+      const int sal = sah - kLoShift;
+      const i32x8 ahi = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+      const i32x8 alo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi, bop[t], acc[mt][t], kFmtE4m3, kFmtE2m1, 0,
+                                                                     sah, 0, sbv[t]);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo, bop[t], acc[mt][t], kFmtE4m3, kFmtE2m1, 0,
+                                                                     sal, 0, sbv[t]);
+    }
+  };
+
+  // full: both steps (the steady state); otherwise the second step runs only
+  // where its blocks exist (the last quad of a K that is an odd count of 64)
+  auto quad = [&](int q, bool more, bool full) {
+    if (more) load_a(q + 1);
+    const uint8_t *Ab = As[q & 1];
+    uint32_t sdw[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sdw[mt] = Asc[q & 1][mt * 32 + n32];
+    step(0, q, Ab, sdw);
+    load_b(0, q + 1);
+    if (full || 4 * q + 2 < T.nkb) step(1, q, Ab, sdw);
+    load_b(1, q + 1);
     if (more) store_a((q + 1) & 1);
     __syncthreads();
   };
 
-  load_bp(0, 0);
-  load_bp(1, 0);
+  load_b(0, 0);
+  load_b(1, 0);
   load_a(0);
   store_a(0);
   __syncthreads();
@@ -269,27 +374,34 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
   int q0 = 0;
   for (; q0 + kUnroll < T.nq; q0 += kUnroll) {
 #pragma unroll
-    for (int d = 0; d < kUnroll; ++d) quad(q0 + d, true);
+    for (int d = 0; d < kUnroll; ++d) quad(q0 + d, true, true);
   }
   // the last one to kUnroll quads
 #pragma unroll
   for (int d = 0; d < kUnroll; ++d)
-    if (q0 + d < T.nq) quad(q0 + d, q0 + d + 1 < T.nq);
+    if (q0 + d < T.nq) quad(q0 + d, q0 + d + 1 < T.nq, false);
 
   // epilogue: acc[mt][t][r] is row mt*32 + 4h + (r%4) + 8(r/4) of the pass, feature f[t]
   const uint16_t *bias = g.bias + (int64_t)T.e * g.bias_stride;
   if (PHASE == 0) {
-    if (T.tile_on[0]) {
+    if (T.tile_on[0]) {  // uniform over the wave: the split reduces over lanes
       const float bg = bf16f(bias[T.f[0]]), bu = bf16f(bias[g.I + T.f[0]]);
+      const int kb4 = kb4_of(g.I), nkb = g.I / 32;
+      const int fb = T.f[0] / 32;  // this wave's 32 features are one k-block of down
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = mt * 32 + 4 * h + (r & 3) + 8 * (r >> 2);
+          const float gv = acc[mt][0][r] + bg, uv = acc[mt][1][r] + bu;
+          const float hv = bf16f(to_bf16(gv / (1.f + __expf(-gv)) * uv));
+          const Split s = split_e4m3(hv);
           if (m < T.mrows) {
-            const float gv = acc[mt][0][r] + bg, uv = acc[mt][1][r] + bu;
-            const float hv = gv / (1.f + __expf(-gv)) * uv;
-            g.hbuf[(int64_t)(T.off + T.m0 + m) * g.I + T.f[0]] = to_bf16(hv);
+            const int64_t row = T.off + T.m0 + m;
+            g.hhi[row * g.I + T.f[0]] = (uint8_t)s.hi;
+            g.hlo[row * g.I + T.f[0]] = (uint8_t)s.lo;
+            if (n32 == 0) g.hsc[row * kb4 + fb] = (uint8_t)s.sbyte;
+            if (fb == nkb - 1 && n32 < kb4 - nkb) g.hsc[row * kb4 + nkb + n32] = 127;
           }
         }
       }
@@ -317,8 +429,9 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
 template <int PHASE>
 __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
   constexpr int NFB = PHASE == 0 ? 128 : 256;  // features per block
-  __shared__ __align__(16) uint16_t As[2][BM * LDA];
-  __shared__ int32_t rowoff[BM];
+  __shared__ __align__(16) uint8_t As[2][BM * LDA];
+  __shared__ uint32_t Asc[2][kThreads];
+  __shared__ int32_t rowidx[BM];
   __shared__ __align__(16) uint8_t sc_lds[kMaxKb * kRowsB];
   Tile T;
   int nt;
@@ -339,6 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
   const int nfeat = PHASE == 0 ? g.I : g.H;
   T.nkb = T.K / 32;
   T.nq = (T.nkb + 3) >> 2;
+  T.kb4 = kb4_of(T.K);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   T.n32 = lane & 31;
   T.h = lane >> 5;
@@ -385,40 +499,42 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int u = 0; u < kScPer; ++u) *reinterpret_cast<uint32_t *>(&sc_lds[(wave + 4 * u) * kRowsB + r4]) = sv[u];
   }
-  const int lda_src = PHASE == 0 ? g.H : g.I;
 
   for (T.m0 = 0; T.m0 < m_e; T.m0 += BM) {
     T.mrows = min(BM, m_e - T.m0);
-    __syncthreads();  // the previous pass is done with rowoff and As; sc_lds is written
+    __syncthreads();  // the previous pass is done with rowidx and As; sc_lds is written
     for (int r = threadIdx.x; r < BM; r += kThreads) {
       int32_t o = -1;
-      if (r < T.mrows) {
-        const int32_t src_row = PHASE == 0 ? g.perm[T.off + T.m0 + r] / g.k : T.off + T.m0 + r;
-        o = src_row * lda_src;
-      }
-      rowoff[r] = o;
+      if (r < T.mrows) o = PHASE == 0 ? g.perm[T.off + T.m0 + r] / g.k : T.off + T.m0 + r;
+      rowidx[r] = o;
     }
     __syncthreads();
     switch ((T.mrows + 31) >> 5) {
-      case 1: gemm_pass<PHASE, 1>(g, T, As, rowoff, sc_lds); break;
-      case 2: gemm_pass<PHASE, 2>(g, T, As, rowoff, sc_lds); break;
-      default: gemm_pass<PHASE, 3>(g, T, As, rowoff, sc_lds); break;
+      case 1: gemm_pass<PHASE, 1>(g, T, As, Asc, rowidx, sc_lds); break;
+      case 2: gemm_pass<PHASE, 2>(g, T, As, Asc, rowidx, sc_lds); break;
+      default: gemm_pass<PHASE, 3>(g, T, As, Asc, rowidx, sc_lds); break;
     }
   }
 }
 
-// ------------------------------------------------------------------ MFMA ceiling
-// Four independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave, the
-// instruction the grouped GEMM uses; operands stay in registers.  The result is
-// stored only on an impossible value, which keeps the chains live.
-__global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *sink) {
+// ------------------------------------------------------------------ MFMA ceilings
+// Four independent accumulator chains per wave with operands in registers; the
+// result is stored only on an impossible value, which keeps the chains live.
+// bf16: v_mfma_f32_32x32x16_bf16.  f8f4: v_mfma_scale_f32_32x32x64_f8f6f4 with
+// A e4m3 and B e2m1, the grouped GEMM's instruction.
+template <bool F8F4>
+__global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *sink, int scale) {
   const int lane = threadIdx.x & 63;
   bf16x8 a, b;
+  i32x8 qa, qb;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     a[i] = (__bf16)(0.001f * (float)(lane + i));
     b[i] = (__bf16)(0.002f * (float)(lane - i));
+    qa[i] = 0x30303030 + lane + i;
+    qb[i] = i < 4 ? 0x21212121 + lane : 0;
   }
+  const int sc = scale + (lane & 1);
   f32x16 acc[kProbeChains];
 #pragma unroll
   for (int c = 0; c < kProbeChains; ++c)
@@ -426,7 +542,12 @@ __global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *
     for (int r = 0; r < 16; ++r) acc[c][r] = (float)(c + r);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int c = 0; c < kProbeChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    for (int c = 0; c < kProbeChains; ++c) {
+      if (F8F4)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, qb, acc[c], kFmtE4m3, kFmtE2m1, 0, sc, 0, sc);
+      else
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
   }
   float t = 0.f;
 #pragma unroll
@@ -460,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, co
 }
 
 struct WsLayout {
-  int64_t offsets, zeros, perm, hbuf, obuf, total;
+  int64_t offsets, zeros, perm, xhi, xlo, xsc, hhi, hlo, hsc, obuf, total;
 };
 
 WsLayout ws_layout(int H, int I, int n, int k, int E) {
@@ -470,21 +591,27 @@ WsLayout ws_layout(int H, int I, int n, int k, int E) {
   L.offsets = 0;
   L.zeros = up(4ll * (E + 1));
   L.perm = L.zeros + 256;
-  L.hbuf = L.perm + up(4 * nk);
-  L.obuf = L.hbuf + up(2 * nk * I);
+  L.xhi = L.perm + up(4 * nk);
+  L.xlo = L.xhi + up((int64_t)n * H);
+  L.xsc = L.xlo + up((int64_t)n * H);
+  L.hhi = L.xsc + up((int64_t)n * kb4_of(H));
+  L.hlo = L.hhi + up(nk * I);
+  L.hsc = L.hlo + up(nk * I);
+  L.obuf = L.hsc + up(nk * kb4_of(I));
   L.total = L.obuf + up(4 * nk * H);
   return L;
 }
 
 }  // namespace
 
-hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t s) {
-  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kThreads), 0, s, iters, sink);
+hipError_t launch_mfma_probe(bool f8f4, int blocks, int iters, float *sink, hipStream_t s) {
+  if (f8f4) hipLaunchKernelGGL(mfma_probe_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, iters, sink, 127);
+  else hipLaunchKernelGGL(mfma_probe_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, iters, sink, 127);
   return hipGetLastError();
 }
 
-int64_t mfma_probe_flops(int blocks, int iters) {
-  return (int64_t)blocks * (kThreads / 64) * iters * kProbeChains * 32 * 32 * 16 * 2;
+int64_t mfma_probe_flops(bool f8f4, int blocks, int iters) {
+  return (int64_t)blocks * (kThreads / 64) * iters * kProbeChains * 32 * 32 * (f8f4 ? 64 : 16) * 2;
 }
 
 bool prefill_supported(int H, int I, int E) {
@@ -495,18 +622,21 @@ int64_t prefill_workspace_bytes(int H, int I, int n, int k, int E) { return ws_l
 
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   if (!prefill_supported(a.H, a.I, a.E)) return hipErrorInvalidValue;
-  // A element offsets of the GEMMs are 32-bit
+  // A byte offsets of the GEMMs (row * K) are 32-bit
   if ((int64_t)a.n * a.k * std::max(a.H, a.I) >= (int64_t)1 << 31) return hipErrorInvalidValue;
   const WsLayout L = ws_layout(a.H, a.I, a.n, a.k, a.E);
   if (a.ws_bytes < L.total) return hipErrorInvalidValue;
   const int nk = a.n * a.k;
   int32_t *offsets = reinterpret_cast<int32_t *>(a.ws + L.offsets);
   int32_t *perm = reinterpret_cast<int32_t *>(a.ws + L.perm);
-  uint16_t *hbuf = reinterpret_cast<uint16_t *>(a.ws + L.hbuf);
-  float *obuf = reinterpret_cast<float *>(a.ws + L.obuf);
   uint32_t *zeros = reinterpret_cast<uint32_t *>(a.ws + L.zeros);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm, zeros);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t xcount = (int64_t)a.n * a.H;
+  hipLaunchKernelGGL(split_kernel, dim3((unsigned)((xcount / 8 + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a.x,
+                     xcount, a.H, a.ws + L.xhi, a.ws + L.xlo, a.ws + L.xsc);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   GemmArgs g;
@@ -517,12 +647,16 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   g.k = a.k;
   g.nk = nk;
   g.xcd = (a.E % kXcds == 0) ? 1 : 0;
-  g.x = a.x;
   g.offsets = offsets;
   g.perm = perm;
-  g.hbuf = hbuf;
-  g.obuf = obuf;
-  // gate_up: banks 0..2; features I, 64 per block
+  g.hhi = a.ws + L.hhi;
+  g.hlo = a.ws + L.hlo;
+  g.hsc = a.ws + L.hsc;
+  g.obuf = reinterpret_cast<float *>(a.ws + L.obuf);
+  // gate_up: banks 0..2, A = the split x; features I, 128 per block
+  g.ahi = a.ws + L.xhi;
+  g.alo = a.ws + L.xlo;
+  g.asc = a.ws + L.xsc;
   g.blocks = a.bank[0];
   g.scales = a.bank[1];
   g.bias = reinterpret_cast<const uint16_t *>(a.bank[2]);
@@ -533,7 +667,10 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(moe_gemm_kernel<0>, dim3(a.E * g.ntiles), dim3(kThreads), 0, s, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // down: banks 3..5; features H
+  // down: banks 3..5, A = the split h; features H, 256 per block
+  g.ahi = g.hhi;
+  g.alo = g.hlo;
+  g.asc = g.hsc;
   g.blocks = a.bank[3];
   g.scales = a.bank[4];
   g.bias = reinterpret_cast<const uint16_t *>(a.bank[5]);
@@ -545,7 +682,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid((a.H / 4 + kThreads - 1) / kThreads, a.n);
-  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, s, obuf, a.ids, a.w, a.n, a.k, a.H, a.E, a.y);
+  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, s, g.obuf, a.ids, a.w, a.n, a.k, a.H, a.E, a.y);
   return hipGetLastError();
 }
 

@@ -113,8 +113,9 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_stream_copy(uint8_t *dst, const uint8_t *src, int64_t bytes, int blocks,
                               hipStream_t s);
 hipError_t launch_hbm_read(const uint8_t *src, int64_t bytes, float *sink, hipStream_t s);
-hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t s);
-int64_t mfma_probe_flops(int blocks, int iters);
+// f8f4: the block-scaled e4m3 x e2m1 MFMA of the prefill GEMM; else the bf16 MFMA
+hipError_t launch_mfma_probe(bool f8f4, int blocks, int iters, float *sink, hipStream_t s);
+int64_t mfma_probe_flops(bool f8f4, int blocks, int iters);
 
 // ---------------------------------------------------------------- debug decode
 // y[i] = bf16_rne(float(y[i]) + add[i]) for i < count (device buffers)

@@ -72,7 +72,10 @@ def test_prefill_ffn_small(H, I, E, k, n, hot):
     err = offn.rel_l2(G.bf16_tensor_to_f64(y), ref)
     print(f"  rel_l2={err:.3e}")
     assert err <= 3e-2
-    assert err <= 1e-2   # bf16 MFMA on exactly dequantised weights: well inside the fp4 bound
+    # the two e4m3 planes hold each bf16 activation exactly and the fp4 weights
+    # enter the MFMA as they are, so what is left is the bf16 rounding of h and
+    # y (about 2^-9 relative each): a plane lost or mis-scaled costs above 1e-2
+    assert err <= 4e-3
     # the buffer holds the layer's bytes
     for b in range(len(hb.banks)):
         assert torch.equal(L.buffer_view(0, b).cpu(), hb.banks[b])
@@ -113,6 +116,7 @@ def test_prefill_full_size_sampled():
     err = offn.rel_l2(G.bf16_tensor_to_f64(y)[sel], ref)
     print(f"  sampled tokens {sel} experts {sorted(experts)} rel_l2={err:.3e}")
     assert err <= 3e-2
+    assert err <= 5e-3   # bf16 rounding of h and y only (exact activation planes)
     # a property at any size: the output is finite and not all zero
     yy = G.bf16_tensor_to_f64(y)
     assert np.isfinite(yy).all() and np.abs(yy).max() > 0
@@ -151,7 +155,7 @@ def test_layer_streaming_double_buffer():
                               lambda e: [hb.row(b, e).numpy() for b in range(len(hb.banks))])
         err = offn.rel_l2(G.bf16_tensor_to_f64(ys[layer]), ref)
         print(f"  layer {layer} rel_l2={err:.3e}")
-        assert err <= 1e-2
+        assert err <= 4e-3
     # an ffn on a layer that is not resident is refused
     with pytest.raises(oes.OesError):
         Lo.ffn(0, x, d_ids, d_w, ys[0], ws, comp)
