@@ -81,6 +81,43 @@ def test_prefill_ffn_small(H, I, E, k, n, hot):
         assert torch.equal(L.buffer_view(0, b).cpu(), hb.banks[b])
 
 
+def test_prefill_ffn_activation_ranges():
+    """The two e4m3 activation planes across value ranges: a zero row, a constant row,
+    rows whose 32-element blocks span 2^30 (beyond the 2^13 exact range), tiny and
+    large magnitudes; the error stays at the bf16 rounding of h and y."""
+    H, I, E, k, n = 192, 128, 8, 2, 48
+    _case(f"prefill ffn activation ranges H={H} I={I} E={E} k={k} n={n}")
+    w = Workload(f"pf-rng-{H}-{I}-{E}", "mxfp4_t", L=1, E=E, k=k, H=H, I=I, S=0)
+    hb = make_host_banks(w)
+    L = _layers(w, hb)
+    L.prefetch(0)
+    logits = synth.router_logits(n, E, 0, w.name).numpy()
+    ids, wts = oroute.topk_softmax(logits, k)
+    rng = np.random.default_rng(7)
+    xf = rng.standard_normal((n, H))
+    xf[0] = 0.0
+    xf[1] = 1.0
+    for r in (2, 3, 4):   # wide dynamic range inside every block
+        xf[r] = np.sign(rng.standard_normal(H)) * np.exp2(rng.uniform(-20.0, 10.0, H))
+    xf[5] = rng.standard_normal(H) * 1e-30
+    xf[6] = rng.standard_normal(H) * 3e2
+    xf[7, ::32] = 5e2      # one large element per block, the rest N(0, 1)
+    x = torch.from_numpy(xf.astype(np.float32)).to(torch.bfloat16).view(torch.int16).to(G.dev())
+    y = _run_ffn(L, 0, x, torch.from_numpy(ids.astype(np.int32)).to(G.dev()),
+                 torch.from_numpy(wts.astype(np.float32)).to(G.dev()))
+    torch.cuda.synchronize()
+    rows = _oracle_rows(hb, None)
+    ref = offn.expert_ffn("mxfp4_t", H, I, G.bits16(x), ids, wts.astype(np.float32).astype(np.float64), rows)
+    got = G.bf16_tensor_to_f64(y)
+    assert np.isfinite(got).all()
+    for r in range(n):
+        e = offn.rel_l2(got[r:r + 1], ref[r:r + 1])
+        assert e <= 6e-3, f"row {r}: rel_l2 {e:.3e}"
+    err = offn.rel_l2(got, ref)
+    print(f"  rel_l2={err:.3e}")
+    assert err <= 4e-3
+
+
 @pytest.mark.timeout(600)
 def test_prefill_full_size_sampled():
     w = WORKLOADS["mxfp4_prefill"]
