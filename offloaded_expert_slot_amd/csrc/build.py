@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-SOURCES = ["api.hip", "k_lru.hip", "k_copy.hip", "k_route.hip", "k_ffn.hip", "k_prefill.hip", "cpu_moe.cpp"]
+SOURCES = ["api.hip", "k_lru.hip", "k_copy.hip", "k_route.hip", "k_ffn.hip", "k_prefill.hip", "cpu_moe.cpp",
+           "host_common.cpp"]
 OUT = os.path.join(PKG, "liboes.so")
 BUILD = os.path.join(HERE, "_build")
 
@@ -26,7 +27,8 @@ FLAGS = [
 ]
 
 
-# host-only sources (the CPU MoE executor): g++, AVX-512 code behind per-function target attributes
+# host-only sources (the CPU MoE executor, the error string and schemas): g++, AVX-512 code
+# behind per-function target attributes
 CXX = os.environ.get("CXX", "g++")
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-I", os.path.join(ROOT, "include")]
 

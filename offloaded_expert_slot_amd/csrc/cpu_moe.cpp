@@ -44,7 +44,7 @@
 #include "oes.h"
 
 namespace oes {
-oes_status set_error(oes_status st, const char *msg);  // api.hip: thread-local message
+oes_status set_error(oes_status st, const char *msg);  // host_common.cpp: thread-local message
 }
 
 namespace {

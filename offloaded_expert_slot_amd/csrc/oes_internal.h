@@ -8,6 +8,9 @@
 
 namespace oes {
 
+// Leaves msg in the thread-local error string read by oes_last_error (host_common.cpp).
+oes_status set_error(oes_status st, const char *msg);
+
 // Device-side control block of one slot cache (one per cache, in HBM).
 struct Ctl {
   uint64_t clock;        // LRU clock: stamp given to the slots of the last step
