@@ -11,7 +11,8 @@
 //                the counts into offsets and scatters the pair indices into
 //                expert order (perm).  The order inside an expert does not
 //                change any result: every output row of a GEMM is computed on
-//                its own, with the same k order.
+//                its own, with the same k order.  It also ranks the experts by
+//                row count, largest first, for the GEMMs' dispatch order.
 //   split      - the bf16 activations x become two e4m3 code planes, hi and lo,
 //                with one power-of-two scale per 32-element block (below).
 //   gemm<0>    - per expert e: h = silu(X_e Wg_e^T + bg) * (X_e Wu_e^T + bu),
@@ -45,9 +46,11 @@
 //   LDS: the K-block-major layout [K/32][N][16 B] gives each lane the 16 bytes
 //   of one MXFP4 block, which is its whole operand of one MFMA step.
 //   Blocks are mapped XCD-aware: hardware deals consecutive block indices to
-//   the 8 XCDs in turn, so block b runs on XCD b % 8; experts e with e % 8 == x
-//   are given to XCD x, which keeps an expert's activation rows in one L2
-//   while all its feature tiles stream their weights.
+//   the 8 XCDs in turn, so block b runs on XCD b % 8; the experts of ranks r
+//   with r % 8 == x are given to XCD x, which keeps an expert's activation rows
+//   in one L2 while all its feature tiles stream their weights.  Ranks follow
+//   row count, largest first: the longest blocks start first on every XCD, and
+//   the tail of the launch holds the shortest ones.
 
 #include <math.h>
 
@@ -86,6 +89,7 @@ struct GemmArgs {
   const uint8_t *asc;    // hi scale bytes [rows, kb4(K)] (lo scale = hi - 4)
   const int32_t *offsets;  // [E + 1]
   const int32_t *perm;     // [nk] pair indices in expert order
+  const int32_t *order;    // [E] experts in dispatch order
   const uint8_t *blocks;   // this phase's _blocks bank, expert stride blocks_stride
   const uint8_t *scales;   // this phase's _scales bank
   const uint16_t *bias;    // this phase's _bias bank (bf16)
@@ -129,7 +133,7 @@ __device__ __forceinline__ Split split_e4m3(float v) {
 
 // ------------------------------------------------------------------ permute
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int nk, int E, int32_t *offsets,
-                                                       int32_t *perm, uint32_t *zeros) {
+                                                       int32_t *perm, int32_t *order, uint32_t *zeros) {
   if (threadIdx.x < 64) zeros[threadIdx.x] = 0u;  // the GEMMs' 256-byte zero source
   __shared__ int hist[OES_MAX_EXPERTS];
   __shared__ int cursor[OES_MAX_EXPERTS];
@@ -153,6 +157,29 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int n
   for (int p = threadIdx.x; p < nk; p += blockDim.x) {
     const int e = ids[p];
     if (e >= 0 && e < E) perm[atomicAdd(&cursor[e], 1)] = p;
+  }
+  // dispatch order of the GEMMs: experts by row count, largest first (ties: lower
+  // index first), so the longest blocks start first; identity past 1024 experts.
+  // Expert e's rank (the experts that come before it) is counted by 1024 / E
+  // threads over slices of the counts; cursor holds their partial counts.
+  __syncthreads();  // the scatter is done with cursor
+  if (E <= 1024) {
+    const int parts = 1024 / E;
+    if ((int)threadIdx.x < E * parts) {
+      const int e = threadIdx.x % E, part = threadIdx.x / E;
+      const int c = hist[e];
+      int cnt = 0;
+      for (int q = E * part / parts; q < E * (part + 1) / parts; ++q) cnt += (hist[q] > c) || (hist[q] == c && q < e);
+      cursor[threadIdx.x] = cnt;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      int rank = 0;
+      for (int part = 0; part < parts; ++part) rank += cursor[part * E + e];
+      order[rank] = e;
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) order[e] = e;
   }
 }
 
@@ -435,15 +462,17 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) uint8_t sc_lds[kMaxKb * kRowsB];
   Tile T;
   int nt;
+  int rank;
   if (g.xcd) {
     const int x = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-    T.e = x + kXcds * (local / g.ntiles);
+    rank = x + kXcds * (local / g.ntiles);
     nt = local % g.ntiles;
   } else {
-    T.e = blockIdx.x / g.ntiles;
+    rank = blockIdx.x / g.ntiles;
     nt = blockIdx.x % g.ntiles;
   }
-  if (T.e >= g.E) return;
+  if (rank >= g.E) return;
+  T.e = g.order[rank];
   T.off = g.offsets[T.e];
   const int m_e = g.offsets[T.e + 1] - T.off;
   if (m_e <= 0) return;
@@ -581,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, co
 }
 
 struct WsLayout {
-  int64_t offsets, zeros, perm, xhi, xlo, xsc, hhi, hlo, hsc, obuf, total;
+  int64_t offsets, order, zeros, perm, xhi, xlo, xsc, hhi, hlo, hsc, obuf, total;
 };
 
 WsLayout ws_layout(int H, int I, int n, int k, int E) {
@@ -589,7 +618,8 @@ WsLayout ws_layout(int H, int I, int n, int k, int E) {
   WsLayout L;
   const int64_t nk = (int64_t)n * k;
   L.offsets = 0;
-  L.zeros = up(4ll * (E + 1));
+  L.order = up(4ll * (E + 1));
+  L.zeros = L.order + up(4ll * E);
   L.perm = L.zeros + 256;
   L.xhi = L.perm + up(4 * nk);
   L.xlo = L.xhi + up((int64_t)n * H);
@@ -629,8 +659,9 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   const int nk = a.n * a.k;
   int32_t *offsets = reinterpret_cast<int32_t *>(a.ws + L.offsets);
   int32_t *perm = reinterpret_cast<int32_t *>(a.ws + L.perm);
+  int32_t *order = reinterpret_cast<int32_t *>(a.ws + L.order);
   uint32_t *zeros = reinterpret_cast<uint32_t *>(a.ws + L.zeros);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm, zeros);
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm, order, zeros);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t xcount = (int64_t)a.n * a.H;
@@ -649,6 +680,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   g.xcd = (a.E % kXcds == 0) ? 1 : 0;
   g.offsets = offsets;
   g.perm = perm;
+  g.order = order;
   g.hhi = a.ws + L.hhi;
   g.hlo = a.ws + L.hlo;
   g.hsc = a.ws + L.hsc;
