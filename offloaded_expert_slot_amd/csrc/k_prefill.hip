@@ -112,7 +112,7 @@ __device__ inline uint16_t to_bf16(float f) {
 }
 
 // Two-plane split of one bf16 value v held by lane (c, half) of a 32-lane half
-// whose lanes hold the 32 elements of one block: every lane of the half must
+// whose lanes hold the 32 elements of one block: every lane of the wave must
 // call it together (the block's largest magnitude is reduced over the half).
 // hi / lo are e4m3 codes, sbyte the hi plane's e8m0 scale byte, kept in
 // [4, 250] so that the lo scale sbyte - 4 is a finite e8m0 value too.
@@ -120,9 +120,19 @@ struct Split {
   uint32_t hi, lo, sbyte;
 };
 __device__ __forceinline__ Split split_e4m3(float v) {
-  uint32_t a = __float_as_uint(v) & 0x7fffffffu;
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+  // block maximum of |v| (as non-negative int bits): a max-scan along each
+  // 16-lane row by DPP row shifts (lanes shifted in from outside the row read
+  // 0, which never wins), after which lane 15 of a row holds the row's maximum;
+  // the four row maxima are read into scalars and each half-wave takes the
+  // larger of its two rows
+  int m = (int)(__float_as_uint(v) & 0x7fffffffu);
+  m = max(m, __builtin_amdgcn_mov_dpp(m, 0x111, 0xf, 0xf, true));  // row_shr:1
+  m = max(m, __builtin_amdgcn_mov_dpp(m, 0x112, 0xf, 0xf, true));  // row_shr:2
+  m = max(m, __builtin_amdgcn_mov_dpp(m, 0x114, 0xf, 0xf, true));  // row_shr:4
+  m = max(m, __builtin_amdgcn_mov_dpp(m, 0x118, 0xf, 0xf, true));  // row_shr:8
+  const int lo_half = max(__builtin_amdgcn_readlane(m, 15), __builtin_amdgcn_readlane(m, 31));
+  const int hi_half = max(__builtin_amdgcn_readlane(m, 47), __builtin_amdgcn_readlane(m, 63));
+  const uint32_t a = (uint32_t)((threadIdx.x & 32) ? hi_half : lo_half);
   const uint32_t sb = (uint32_t)min(max((int)(a >> 23) - 7, 4), 250);
   const float xs = v * __uint_as_float((254u - sb) << 23);  // v / 2^(sb - 127), exact
   const uint32_t hp = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xs, 0.f, 0, false);
