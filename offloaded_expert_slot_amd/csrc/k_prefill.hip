@@ -141,6 +141,18 @@ __device__ __forceinline__ Split split_e4m3(float v) {
   return {hp & 0xffu, lp & 0xffu, sb};
 }
 
+// 4x4 byte transpose inside each quad of lanes: lane c (= lane % 4) of the quad
+// passes p, whose byte r belongs to row r; it receives the bytes c of the four
+// lanes' p, lane c' in byte c'.
+__device__ __forceinline__ uint32_t quad_transpose(uint32_t p, int c) {
+  const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0xb1, 0xf, 0xf, false);  // quad_perm 1,0,3,2
+  const uint32_t p2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0x4e, 0xf, 0xf, false);  // quad_perm 2,3,0,1
+  const uint32_t p3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0x1b, 0xf, 0xf, false);  // quad_perm 3,2,1,0
+  const int sh = 8 * c;
+  return (((p >> sh) & 0xffu) << (8 * c)) | (((p1 >> sh) & 0xffu) << (8 * (c ^ 1))) |
+         (((p2 >> sh) & 0xffu) << (8 * (c ^ 2))) | (((p3 >> sh) & 0xffu) << (8 * (c ^ 3)));
+}
+
 // ------------------------------------------------------------------ permute
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int nk, int E, int32_t *offsets,
                                                        int32_t *perm, int32_t *order, uint32_t *zeros) {
@@ -425,20 +437,37 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
       const float bg = bf16f(bias[T.f[0]]), bu = bf16f(bias[g.I + T.f[0]]);
       const int kb4 = kb4_of(g.I), nkb = g.I / 32;
       const int fb = T.f[0] / 32;  // this wave's 32 features are one k-block of down
+      // lane quad (4q .. 4q + 3) holds rows m .. m + 3 (r = 4rq + 0..3) of features
+      // 4q .. 4q + 3; after a 4x4 byte transpose inside the quad, lane c holds the
+      // four features of row m + c as one dword
+      const int c = n32 & 3;
+      const int fcol = T.f[0] & ~3;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mt * 32 + 4 * h + (r & 3) + 8 * (r >> 2);
-          const float gv = acc[mt][0][r] + bg, uv = acc[mt][1][r] + bu;
-          const float hv = bf16f(to_bf16(gv / (1.f + __expf(-gv)) * uv));
-          const Split s = split_e4m3(hv);
+        for (int rq = 0; rq < 4; ++rq) {
+          uint32_t ph = 0, pl = 0, sc = 0;
+#pragma unroll
+          for (int r3 = 0; r3 < 4; ++r3) {
+            const int r = 4 * rq + r3;
+            const float gv = acc[mt][0][r] + bg, uv = acc[mt][1][r] + bu;
+            const float hv = bf16f(to_bf16(gv / (1.f + __expf(-gv)) * uv));
+            const Split s = split_e4m3(hv);
+            ph |= s.hi << (8 * r3);
+            pl |= s.lo << (8 * r3);
+            sc = r3 == c ? s.sbyte : sc;
+          }
+          const uint32_t th = quad_transpose(ph, c), tl = quad_transpose(pl, c);
+          const int m = mt * 32 + 4 * h + 8 * rq + c;
           if (m < T.mrows) {
             const int64_t row = T.off + T.m0 + m;
-            g.hhi[row * g.I + T.f[0]] = (uint8_t)s.hi;
-            g.hlo[row * g.I + T.f[0]] = (uint8_t)s.lo;
-            if (n32 == 0) g.hsc[row * kb4 + fb] = (uint8_t)s.sbyte;
-            if (fb == nkb - 1 && n32 < kb4 - nkb) g.hsc[row * kb4 + nkb + n32] = 127;
+            *reinterpret_cast<uint32_t *>(g.hhi + row * g.I + fcol) = th;
+            *reinterpret_cast<uint32_t *>(g.hlo + row * g.I + fcol) = tl;
+            if (n32 < 4) {  // one lane per row writes its scale byte (and the pad past K / 32)
+              g.hsc[row * kb4 + fb] = (uint8_t)sc;
+              if (fb == nkb - 1)
+                for (int j = nkb; j < kb4; ++j) g.hsc[row * kb4 + j] = 127;
+            }
           }
         }
       }
