@@ -11,16 +11,17 @@
 //                the counts into offsets and scatters the pair indices into
 //                expert order (perm).  The order inside an expert does not
 //                change any result: every output row of a GEMM is computed on
-//                its own, with the same k order.  It also ranks the experts by
-//                row count, largest first, for the GEMMs' dispatch order.
+//                its own, with the same k order.  It also records each pair's
+//                position in expert order (pos) and ranks the experts by row
+//                count, largest first, for the GEMMs' dispatch order.
 //   split      - the bf16 activations x become two e4m3 code planes, hi and lo,
 //                with one power-of-two scale per 32-element block (below).
 //   gemm<0>    - per expert e: h = silu(X_e Wg_e^T + bg) * (X_e Wu_e^T + bu),
 //                rounded to bf16 and split like x, X_e the gathered activation
 //                rows of the pairs routed to e.
-//   gemm<1>    - per expert e: o = h_e Wd_e^T + bd, fp32, scattered back to the
-//                pair's row.
-//   combine    - y_t = sum_j w[t, j] * o_{t,j} in pair order, bf16.
+//   gemm<1>    - per expert e: o = h_e Wd_e^T + bd, fp32, rows in expert order.
+//   combine    - y_t = sum_j w[t, j] * o_{t,j} in pair order, bf16, each pair's
+//                row found through its expert-order position (pos).
 //
 // Exact two-plane activations.  The weights stay MXFP4 (e2m1 codes with an e8m0
 // scale per 32 k) and go to v_mfma_scale_f32_32x32x64_f8f6f4 as they are, with
@@ -97,7 +98,7 @@ struct GemmArgs {
   const u32x4 *zero16;   // 16 zero bytes: the source of A pieces past K
   uint8_t *hhi, *hlo;    // gate_up output h: e4m3 planes [nk, I], expert order
   uint8_t *hsc;          // its hi scale bytes [nk, kb4(I)]
-  float *obuf;           // [nk, H] fp32, pair order
+  float *obuf;           // [nk, H] fp32, expert order
 };
 
 // scale bytes per row of a split plane: K / 32 rounded up to whole quads of four
@@ -155,7 +156,8 @@ __device__ __forceinline__ uint32_t quad_transpose(uint32_t p, int c) {
 
 // ------------------------------------------------------------------ permute
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int nk, int E, int32_t *offsets,
-                                                       int32_t *perm, int32_t *order, uint32_t *zeros) {
+                                                       int32_t *perm, int32_t *pos, int32_t *order,
+                                                       uint32_t *zeros) {
   if (threadIdx.x < 64) zeros[threadIdx.x] = 0u;  // the GEMMs' 256-byte zero source
   __shared__ int hist[OES_MAX_EXPERTS];
   __shared__ int cursor[OES_MAX_EXPERTS];
@@ -178,7 +180,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int n
   __syncthreads();
   for (int p = threadIdx.x; p < nk; p += blockDim.x) {
     const int e = ids[p];
-    if (e >= 0 && e < E) perm[atomicAdd(&cursor[e], 1)] = p;
+    int at = -1;
+    if (e >= 0 && e < E) {
+      at = atomicAdd(&cursor[e], 1);
+      perm[at] = p;
+    }
+    pos[p] = at;  // the pair's row in expert order (-1: skipped)
   }
   // dispatch order of the GEMMs: experts by row count, largest first (ties: lower
   // index first), so the longest blocks start first; identity past 1024 experts.
@@ -482,10 +489,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = mt * 32 + 4 * h + (r & 3) + 8 * (r >> 2);
-          if (m < T.mrows) {
-            const int pr = g.perm[T.off + T.m0 + m];
-            g.obuf[(int64_t)pr * g.H + T.f[t]] = acc[mt][t][r] + bd;
-          }
+          if (m < T.mrows) g.obuf[(int64_t)(T.off + T.m0 + m) * g.H + T.f[t]] = acc[mt][t][r] + bd;
         }
       }
     }
@@ -624,9 +628,10 @@ __global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *
 }
 
 // ------------------------------------------------------------------ combine
-// y[t, c..c+3] = sum_j w[t, j] * o[t*k + j, c..c+3], pairs with an invalid id skipped.
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, const int32_t *ids, const float *w, int n,
-                                                           int k, int H, int E, uint16_t *y) {
+// y[t, c..c+3] = sum_j w[t, j] * o[pos[t*k + j], c..c+3] (o in expert order), pairs
+// with an invalid id skipped.
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, const int32_t *pos, const int32_t *ids,
+                                                           const float *w, int n, int k, int H, int E, uint16_t *y) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * kThreads + threadIdx.x) * 4;
   if (t >= n || c >= H) return;
@@ -636,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, co
     const int e = ids[p];
     if (e < 0 || e >= E) continue;
     const float wj = w[p];
-    const f32x4 o = *reinterpret_cast<const f32x4 *>(obuf + (int64_t)p * H + c);
+    const f32x4 o = *reinterpret_cast<const f32x4 *>(obuf + (int64_t)pos[p] * H + c);
     s[0] = fmaf(wj, o[0], s[0]);
     s[1] = fmaf(wj, o[1], s[1]);
     s[2] = fmaf(wj, o[2], s[2]);
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, co
 }
 
 struct WsLayout {
-  int64_t offsets, order, zeros, perm, xhi, xlo, xsc, hhi, hlo, hsc, obuf, total;
+  int64_t offsets, order, zeros, perm, pos, xhi, xlo, xsc, hhi, hlo, hsc, obuf, total;
 };
 
 WsLayout ws_layout(int H, int I, int n, int k, int E) {
@@ -660,7 +665,8 @@ WsLayout ws_layout(int H, int I, int n, int k, int E) {
   L.order = up(4ll * (E + 1));
   L.zeros = L.order + up(4ll * E);
   L.perm = L.zeros + 256;
-  L.xhi = L.perm + up(4 * nk);
+  L.pos = L.perm + up(4 * nk);
+  L.xhi = L.pos + up(4 * nk);
   L.xlo = L.xhi + up((int64_t)n * H);
   L.xsc = L.xlo + up((int64_t)n * H);
   L.hhi = L.xsc + up((int64_t)n * kb4_of(H));
@@ -699,8 +705,9 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   int32_t *offsets = reinterpret_cast<int32_t *>(a.ws + L.offsets);
   int32_t *perm = reinterpret_cast<int32_t *>(a.ws + L.perm);
   int32_t *order = reinterpret_cast<int32_t *>(a.ws + L.order);
+  int32_t *pos = reinterpret_cast<int32_t *>(a.ws + L.pos);
   uint32_t *zeros = reinterpret_cast<uint32_t *>(a.ws + L.zeros);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm, order, zeros);
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm, pos, order, zeros);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t xcount = (int64_t)a.n * a.H;
@@ -753,7 +760,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid((a.H / 4 + kThreads - 1) / kThreads, a.n);
-  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, s, g.obuf, a.ids, a.w, a.n, a.k, a.H, a.E, a.y);
+  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(kThreads), 0, s, g.obuf, pos, a.ids, a.w, a.n, a.k, a.H, a.E, a.y);
   return hipGetLastError();
 }
 
