@@ -458,7 +458,9 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
           for (int r3 = 0; r3 < 4; ++r3) {
             const int r = 4 * rq + r3;
             const float gv = acc[mt][0][r] + bg, uv = acc[mt][1][r] + bu;
-            const float hv = bf16f(to_bf16(gv / (1.f + __expf(-gv)) * uv));
+            // silu(g) * u with the hardware reciprocal (about 1 ulp; h is rounded to
+            // bf16 next, by the hardware conversion, round to nearest even)
+            const float hv = (float)(__bf16)(gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv);
             const Split s = split_e4m3(hv);
             ph |= s.hi << (8 * r3);
             pl |= s.lo << (8 * r3);
