@@ -50,6 +50,8 @@ def _oracle_rows(hb, sel_ids):
     (128, 192, 16, 4, 100, None),       # ragged groups, several feature tiles
     (192, 128, 12, 2, 70, None),        # E not a multiple of 8: plain block mapping
     (128, 128, 8, 2, 300, 3),           # one expert gets every token: 3 passes of 128 rows
+    (64, 128, 1024, 4, 300, None),      # dispatch order ranked over 1024 experts, one quad of K
+    (64, 64, 1100, 2, 200, None),       # past 1024 experts: dispatch in index order
 ])
 def test_prefill_ffn_small(H, I, E, k, n, hot):
     _case(f"prefill ffn H={H} I={I} E={E} k={k} n={n} hot={hot}")
