@@ -19,14 +19,16 @@ Also printed (same JSON line): the copy sweep of the benchmark guide's columns
 (bs, active, miss_rate, misses, time_ms, copy_MiB, bw_GBps, tok_ms; median of
 25 event-timed ensure+copy repeats, fused and per-bank), decode tok/s at every
 miss rate, the measured ceilings (pinned H2D by DMA and by the zero-copy
-kernel, HBM streaming read, bf16 MFMA loop), the roofline of the dominant kernel and of the
-FFN, copy_missing of every decode bank format (8 misses), the hybrid backend (host DRAM read and link ceilings, the CPU MoE
-executor and the PCIe gather alone and overlapped, the decision and fetch
-split, the hybrid decode layer step beside the offload one), the cold decode
-FFN of every decode bank format (bf16, fp8 block, nvfp4,
-GGUF Q4_0) at its workload's shape, a slot-pool resize (half the slots and back),
-the MXFP4 prefill layer (grouped FFN on MFMA, whole-layer stream, the
-overlapped loop over 4 layers) and the CPU oracle timed on this host.
+kernel, HBM streaming read, the bf16 and the block-scaled e4m3 x e2m1 MFMA
+loops), the roofline of the dominant kernel and of the FFN, copy_missing of
+every decode bank format (8 misses), the hybrid backend (host DRAM read and
+link ceilings, the CPU MoE executor and the PCIe gather alone and overlapped,
+the decision and fetch split, the hybrid decode layer step beside the offload
+one), the cold decode FFN of every decode bank format (bf16, fp8 block, nvfp4,
+GGUF Q4_0) at its workload's shape, a slot-pool resize (half the slots and
+back), the MXFP4 prefill layer (grouped FFN on the block-scaled MFMA,
+whole-layer stream, the overlapped loop over 4 layers) and the CPU oracle timed
+on this host.
 """
 import argparse
 import json
