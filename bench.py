@@ -162,6 +162,7 @@ def main():
             cache.load_rows([p[0] for p in pre], [p[1] for p in pre])
         cache.snapshot()
         torch.cuda.synchronize()
+        _hold_gpu(0.2 * (warmup + steps))
         rec = []
         for i in range(warmup + steps):
             cache.restore()
@@ -227,6 +228,8 @@ def main():
         cache.expert_ffn(x, maps[i], wts, y, fws)
     a, b = ev(), ev()
     n_ffn = 64
+    torch.cuda.synchronize()
+    _hold_gpu(5.0)
     a.record(stream)
     for i in range(n_ffn):
         cache.expert_ffn(x, maps[i % nsets], wts, y, fws)
@@ -644,6 +647,8 @@ def _ffn_formats(workloads, nsets, launches, probes, log):
         for i in range(4):
             c.expert_ffn(x, maps[i], wts, y, ws)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        _hold_gpu(5.0)
         a.record(stream)
         for i in range(launches):
             c.expert_ffn(x, maps[i % nsets], wts, y, ws)
@@ -680,6 +685,26 @@ def _pmc_traffic(kernel):
                     return int(kv["bytes_per_launch"])
                 return None
     return None
+
+
+_HOLD = {}
+
+
+def _hold_gpu(ms):
+    """Keep the current stream busy for about `ms` milliseconds with a spinning
+    kernel, so that the host enqueues the timed launches that follow before the
+    GPU reaches them: the events then time the GPU work alone, not the host's
+    launch rate (which can be the slower of the two for microsecond kernels).
+    The spin itself lies before the first event."""
+    import torch
+    if "cycles_per_ms" not in _HOLD:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1 << 20)
+        b.record()
+        b.synchronize()
+        _HOLD["cycles_per_ms"] = (1 << 20) / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_HOLD["cycles_per_ms"] * ms))
 
 
 def _prefill(w, log):
