@@ -19,7 +19,8 @@
 //   gemm<0>    - per expert e: h = silu(X_e Wg_e^T + bg) * (X_e Wu_e^T + bu),
 //                rounded to bf16 and split like x, X_e the gathered activation
 //                rows of the pairs routed to e.
-//   gemm<1>    - per expert e: o = h_e Wd_e^T + bd, fp32, rows in expert order.
+//   gemm<1>    - per expert e: o = h_e Wd_e^T + bd, rounded to bf16 (as h is
+//                between the GEMMs), rows in expert order.
 //   combine    - y_t = sum_j w[t, j] * o_{t,j} in pair order, bf16, each pair's
 //                row found through its expert-order position (pos).
 //
@@ -98,7 +99,7 @@ struct GemmArgs {
   const u32x4 *zero16;   // 16 zero bytes: the source of A pieces past K
   uint8_t *hhi, *hlo;    // gate_up output h: e4m3 planes [nk, I], expert order
   uint8_t *hsc;          // its hi scale bytes [nk, kb4(I)]
-  float *obuf;           // [nk, H] fp32, expert order
+  uint16_t *obuf;        // [nk, H] bf16, expert order
 };
 
 // scale bytes per row of a split plane: K / 32 rounded up to whole quads of four
@@ -491,7 +492,9 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = mt * 32 + 4 * h + (r & 3) + 8 * (r >> 2);
-          if (m < T.mrows) g.obuf[(int64_t)(T.off + T.m0 + m) * g.H + T.f[t]] = acc[mt][t][r] + bd;
+          if (m < T.mrows)
+            g.obuf[(int64_t)(T.off + T.m0 + m) * g.H + T.f[t]] =
+                __builtin_bit_cast(uint16_t, (__bf16)(acc[mt][t][r] + bd));
         }
       }
     }
@@ -630,9 +633,9 @@ __global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *
 }
 
 // ------------------------------------------------------------------ combine
-// y[t, c..c+3] = sum_j w[t, j] * o[pos[t*k + j], c..c+3] (o in expert order), pairs
-// with an invalid id skipped.
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, const int32_t *pos, const int32_t *ids,
+// y[t, c..c+3] = sum_j w[t, j] * o[pos[t*k + j], c..c+3] (o bf16 in expert order, the
+// sum in fp32), pairs with an invalid id skipped.
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t *obuf, const int32_t *pos, const int32_t *ids,
                                                            const float *w, int n, int k, int H, int E, uint16_t *y) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -643,7 +646,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *obuf, co
     const int e = ids[p];
     if (e < 0 || e >= E) continue;
     const float wj = w[p];
-    const f32x4 o = *reinterpret_cast<const f32x4 *>(obuf + (int64_t)pos[p] * H + c);
+    const u32x2 ob = *reinterpret_cast<const u32x2 *>(obuf + (int64_t)pos[p] * H + c);
+    const f32x4 o = {__uint_as_float(ob[0] << 16), __uint_as_float(ob[0] & 0xffff0000u), __uint_as_float(ob[1] << 16),
+                     __uint_as_float(ob[1] & 0xffff0000u)};
     s[0] = fmaf(wj, o[0], s[0]);
     s[1] = fmaf(wj, o[1], s[1]);
     s[2] = fmaf(wj, o[2], s[2]);
@@ -675,7 +680,7 @@ WsLayout ws_layout(int H, int I, int n, int k, int E) {
   L.hlo = L.hhi + up(nk * I);
   L.hsc = L.hlo + up(nk * I);
   L.obuf = L.hsc + up(nk * kb4_of(I));
-  L.total = L.obuf + up(4 * nk * H);
+  L.total = L.obuf + up(2 * nk * H);
   return L;
 }
 
@@ -732,7 +737,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   g.hhi = a.ws + L.hhi;
   g.hlo = a.ws + L.hlo;
   g.hsc = a.ws + L.hsc;
-  g.obuf = reinterpret_cast<float *>(a.ws + L.obuf);
+  g.obuf = reinterpret_cast<uint16_t *>(a.ws + L.obuf);
   // gate_up: banks 0..2, A = the split x; features I, 128 per block
   g.ahi = a.ws + L.xhi;
   g.alo = a.ws + L.xlo;
