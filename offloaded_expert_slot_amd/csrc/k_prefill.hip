@@ -6,7 +6,7 @@
 // expert e).  FreeToken MoE benchmark guide §4.2: the MXFP4 format keeps six
 // transposed banks - _blocks, _scales, _bias for gate_up and for down.
 //
-// Five launches:
+// Four launches (permute and split share the first):
 //   permute    - one workgroup counts the (token, pair) routes per expert, scans
 //                the counts into offsets and scatters the pair indices into
 //                expert order (perm).  The order inside an expert does not
@@ -156,9 +156,9 @@ __device__ __forceinline__ uint32_t quad_transpose(uint32_t p, int c) {
 }
 
 // ------------------------------------------------------------------ permute
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int nk, int E, int32_t *offsets,
-                                                       int32_t *perm, int32_t *pos, int32_t *order,
-                                                       uint32_t *zeros) {
+// Run by one workgroup of 1024 threads.
+__device__ __forceinline__ void permute_body(const int32_t *ids, int nk, int E, int32_t *offsets, int32_t *perm,
+                                             int32_t *pos, int32_t *order, uint32_t *zeros) {
   if (threadIdx.x < 64) zeros[threadIdx.x] = 0u;  // the GEMMs' 256-byte zero source
   __shared__ int hist[OES_MAX_EXPERTS];
   __shared__ int cursor[OES_MAX_EXPERTS];
@@ -220,9 +220,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *ids, int n
 // straddle rows and count = rows * K is a multiple of 32: each group of four
 // lanes is wholly in or out).  The scale bytes past K / 32 (up to the quad) get
 // 127 (scale 1): the GEMMs multiply them by zero codes only.
-__global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t *x, int64_t count, int K, uint8_t *hi,
-                                                         uint8_t *lo, uint8_t *sc) {
-  const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+// Lane `lane` (of the whole launch's split lanes) takes elements 8 lane .. 8 lane + 7.
+__device__ __forceinline__ void split_body(const uint16_t *x, int64_t count, int K, uint8_t *hi, uint8_t *lo,
+                                           uint8_t *sc, int64_t lane) {
+  const int64_t i = lane * 8;
   if (i >= count) return;
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + i));
   float f[8];
@@ -258,6 +259,29 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t *x, int6
   if ((col & 31) == 0) sc[row * kb4 + col / 32] = (uint8_t)sb;
   if (col == 0)
     for (int j = nkb; j < kb4; ++j) sc[row * kb4 + j] = 127;
+}
+
+// ------------------------------------------------------------------ prep
+// permute and split are independent: one launch runs both, block 0 permuting the
+// pairs while blocks 1.. split x, so the single-workgroup permute hides behind
+// the split instead of adding its time.
+struct PrepArgs {
+  const int32_t *ids;
+  int nk, E;
+  int32_t *offsets, *perm, *pos, *order;
+  uint32_t *zeros;
+  const uint16_t *x;
+  int64_t count;
+  int K;
+  uint8_t *hi, *lo, *sc;
+};
+constexpr int kPrepThreads = 1024;
+
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
+  if (blockIdx.x == 0)
+    permute_body(a.ids, a.nk, a.E, a.offsets, a.perm, a.pos, a.order, a.zeros);
+  else
+    split_body(a.x, a.count, a.K, a.hi, a.lo, a.sc, (int64_t)(blockIdx.x - 1) * kPrepThreads + threadIdx.x);
 }
 
 // ------------------------------------------------------------------ grouped GEMM
@@ -714,13 +738,24 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t s) {
   int32_t *order = reinterpret_cast<int32_t *>(a.ws + L.order);
   int32_t *pos = reinterpret_cast<int32_t *>(a.ws + L.pos);
   uint32_t *zeros = reinterpret_cast<uint32_t *>(a.ws + L.zeros);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, a.ids, nk, a.E, offsets, perm, pos, order, zeros);
+  PrepArgs pa;
+  pa.ids = a.ids;
+  pa.nk = nk;
+  pa.E = a.E;
+  pa.offsets = offsets;
+  pa.perm = perm;
+  pa.pos = pos;
+  pa.order = order;
+  pa.zeros = zeros;
+  pa.x = a.x;
+  pa.count = (int64_t)a.n * a.H;
+  pa.K = a.H;
+  pa.hi = a.ws + L.xhi;
+  pa.lo = a.ws + L.xlo;
+  pa.sc = a.ws + L.xsc;
+  const int64_t split_blocks = (pa.count / 8 + kPrepThreads - 1) / kPrepThreads;
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(1 + split_blocks)), dim3(kPrepThreads), 0, s, pa);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t xcount = (int64_t)a.n * a.H;
-  hipLaunchKernelGGL(split_kernel, dim3((unsigned)((xcount / 8 + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a.x,
-                     xcount, a.H, a.ws + L.xhi, a.ws + L.xlo, a.ws + L.xsc);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   GemmArgs g;
