@@ -401,7 +401,10 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
   };
 
   // one 64-k step: per m-tile, the hi plane's MFMAs on both n-tiles, then the lo plane's
+  // the wave issues a step's MFMAs at raised priority, so that of the two waves
+  // sharing a SIMD the one with operands ready keeps the matrix pipe fed
   auto step = [&](int j, int q, const uint8_t *Ab, const uint32_t *sdw) {
+    __builtin_amdgcn_s_setprio(1);
     const uint8_t *sl = sc_lds + step_kb0(j, q) * kRowsB;
     int sbv[NTW];
     i32x8 bop[NTW];
@@ -428,6 +431,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
         acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo, bop[t], acc[mt][t], kFmtE4m3, kFmtE2m1, 0,
                                                                      sal, 0, sbv[t]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // full: both steps (the steady state); otherwise the second step runs only
