@@ -401,10 +401,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
   };
 
   // one 64-k step: per m-tile, the hi plane's MFMAs on both n-tiles, then the lo plane's
-  // the wave issues a step's MFMAs at raised priority, so that of the two waves
-  // sharing a SIMD the one with operands ready keeps the matrix pipe fed
   auto step = [&](int j, int q, const uint8_t *Ab, const uint32_t *sdw) {
-    __builtin_amdgcn_s_setprio(1);
     const uint8_t *sl = sc_lds + step_kb0(j, q) * kRowsB;
     int sbv[NTW];
     i32x8 bop[NTW];
@@ -431,12 +428,15 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
         acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo, bop[t], acc[mt][t], kFmtE4m3, kFmtE2m1, 0,
                                                                      sal, 0, sbv[t]);
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // full: both steps (the steady state); otherwise the second step runs only
   // where its blocks exist (the last quad of a K that is an odd count of 64)
+  // a quad's loads and MFMAs are issued at raised wave priority, lowered again
+  // for the barrier, so that of the two waves sharing a SIMD the one still
+  // working keeps the matrix pipe fed while the other waits
   auto quad = [&](int q, bool more, bool full) {
+    __builtin_amdgcn_s_setprio(1);
     if (more) load_a(q + 1);
     const uint8_t *Ab = As[q & 1];
     uint32_t sdw[MT];
@@ -447,6 +447,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs &g, const Tile &T, uint
     if (full || 4 * q + 2 < T.nkb) step(1, q, Ab, sdw);
     load_b(1, q + 1);
     if (more) store_a((q + 1) & 1);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   };
 
