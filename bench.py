@@ -190,6 +190,7 @@ def main():
 
     per_mr = []
     headline = None
+    gpu_step = None
     # the headline miss rate runs first, so that its copy launches are the first
     # gather dispatches of the run: 0..W+K-1 the timed pass, W+K..2(W+K)-1 the
     # breakdown pass (the profile summary averages the latter's timed ones)
@@ -212,6 +213,12 @@ def main():
         per_mr.sort(key=lambda r: r["miss_rate"])
         if is_head:
             headline = (row, total, parts)
+            # the step's outputs (every step of the loop starts from the same state)
+            gm = cache.get_misses()
+            gslots = torch.tensor([m[0] for m in gm], dtype=torch.long, device=dev)
+            gpu_step = {"ids": ids.cpu().numpy().copy(), "slot_ids": slot_ids.cpu().numpy().copy(),
+                        "y": y.view(torch.bfloat16).double().cpu().numpy(), "misses": gm,
+                        "rows": [cache.slot_bank_view(b)[gslots].cpu().numpy() for b in range(len(hb.banks))]}
         log("decode", {k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()})
 
     # FFN alone (HBM roofline): back-to-back launches, each on one of 16 slot maps
@@ -338,7 +345,9 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = _cpu_baseline(w, hb, x, wg, args.miss_rate, args.cpu_seconds)
+        cpu = _cpu_baseline(w, hb, x, wg, args.miss_rate, args.cpu_seconds, gpu_step)
+        if cpu["parity"] is not None and not cpu["parity"]["ok"]:
+            log("PARITY FAILED: the GPU step differs from the oracle", cpu["parity"])
         log("cpu_baseline", cpu)
 
     ms = head["ms_per_step"]
@@ -352,9 +361,16 @@ def main():
         "tok_ms": head["tok_ms"], "copy_GBps": head.get("copy_GBps"),
         "roofline": roof, "kernels": kernels, "probes": probes, "decode_per_miss_rate": per_mr,
         "copy_sweep": sweep, "ffn_formats": ffn_formats, "copy_formats": copy_formats, "hybrid": hybrid, "resize": resize, "prefill": prefill,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu, "parity": cpu["parity"] if cpu else None,
     }
+    parity_failed = bool(cpu and cpu["parity"] is not None and not cpu["parity"]["ok"])
+    if parity_failed:
+        # a number from a step that does not match the oracle is not reported
+        out["value"] = None
+        out["invalid"] = "the headline step differs from the oracle (see parity)"
     print(json.dumps(out), flush=True)
+    if parity_failed:
+        sys.exit(1)
     cache.close()
 
 
@@ -769,8 +785,13 @@ def _prefill(w, log):
     return out
 
 
-def _cpu_baseline(w, hb, x, wg, mr, budget_s):
-    """The oracle, as it stands, on this host: route + LRU + row copies + FFN for bs=1 steps."""
+def _cpu_baseline(w, hb, x, wg, mr, budget_s, gpu_step=None):
+    """The oracle, as it stands, on this host: route + LRU + row copies + FFN for bs=1 steps.
+
+    Its first step also gates the GPU numbers: the routed ids, the slot map, the
+    (slot, expert id) misses and the bytes those misses copied into the slot banks in
+    the headline step must equal the oracle's, and its FFN output must be within the
+    format's tolerance (relative L2 <= 1e-2, 3e-2 for fp4 banks) of the oracle's."""
     import numpy as np
 
     import synth
@@ -788,6 +809,7 @@ def _cpu_baseline(w, hb, x, wg, mr, budget_s):
     host = [[hb.banks[b].numpy().reshape(w.E, -1)] for b in range(len(hb.banks))]
     mirror = [np.zeros((w.S, rb), dtype=np.uint8) for rb in hb.row_bytes]
     times = []
+    first = None
     t_start = time.perf_counter()
     while not times or (time.perf_counter() - t_start < budget_s and len(times) < 25):
         t0 = time.perf_counter()
@@ -799,15 +821,31 @@ def _cpu_baseline(w, hb, x, wg, mr, budget_s):
         t1 = time.perf_counter()
         r = t.ensure(0, ids)
         ocopy.copy_missing(r.misses, host, mirror, w.E)
-        offn.expert_ffn(w.fmt, w.H, w.I, xb, r.slot_ids, wts,
-                        lambda s: [host[b][0][int(t.owner[s]) % w.E] for b in range(len(host))])
+        yo = offn.expert_ffn(w.fmt, w.H, w.I, xb, r.slot_ids, wts,
+                             lambda s: [host[b][0][int(t.owner[s]) % w.E] for b in range(len(host))])
         t2 = time.perf_counter()
         times.append(((t2 - t1) + (t1 - t0)) * 1000.0)
+        if first is None:
+            ms_ = sorted((int(sl), int(e)) for sl, e in r.misses)
+            first = (ids, r.slot_ids, yo, ms_, [m[[sl for sl, _ in ms_]].copy() for m in mirror])
     ms = float(np.median(times))
+    parity = None
+    if gpu_step is not None:
+        ids_ok = bool(np.array_equal(gpu_step["ids"], first[0]))
+        slots_ok = bool(np.array_equal(gpu_step["slot_ids"], first[1]))
+        order = np.argsort([sl for sl, _ in gpu_step["misses"]], kind="stable")
+        gmiss = [tuple(gpu_step["misses"][i]) for i in order]
+        miss_ok = gmiss == first[3]
+        bytes_ok = miss_ok and all(np.array_equal(g[order], o) for g, o in zip(gpu_step["rows"], first[4]))
+        err = float(offn.rel_l2(gpu_step["y"], first[2]))
+        tol = 3e-2 if w.fmt in ("nvfp4", "q4_0") else 1e-2
+        parity = {"ids": ids_ok, "slot_ids": slots_ok, "misses": miss_ok, "slot_bytes": bytes_ok,
+                  "ffn_rel_l2": err, "ffn_tol": tol,
+                  "ok": ids_ok and slots_ok and miss_ok and bytes_ok and err <= tol}
     return {"value": 1000.0 / (w.L * ms), "unit": "tok/s", "cores": int(blas_threads), "kind": "oracle",
             "ms_per_step": ms, "sample": f"{len(times)} bs=1 decode steps of {w.name} at miss_rate {mr} "
                                         f"(route, LRU, row copies, float64 FFN), median",
-            "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+            "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "parity": parity}
 
 
 if __name__ == "__main__":
