@@ -345,7 +345,9 @@ oes_status oes_layers_buffer(const oes_layers *p, int32_t index, int32_t bank, v
 oes_status oes_layers_ffn_workspace(const oes_layers *p, int32_t n, int32_t k, int64_t *bytes);
 /* Grouped expert FFN of layer `layer` (which must have been prefetched) over
  * n tokens routed to ids [n, k] int32 device with weights w [n, k] float
- * device: y [n, H] bf16.  Format: OES_MXFP4_T (MFMA grouped GEMM).  Async. */
+ * device: y [n, H] bf16.  An id outside [0, E) (-1, say) skips its pair; a
+ * token whose pairs are all skipped gets y = 0; n = 0 launches nothing.
+ * Format: OES_MXFP4_T (MFMA grouped GEMM).  Async. */
 oes_status oes_layers_ffn(oes_layers *p, int32_t layer, const void *x, const int32_t *ids,
                           const float *w, int32_t n, int32_t k, void *y, void *workspace,
                           int64_t workspace_bytes, void *compute_stream);

@@ -84,6 +84,44 @@ def test_prefill_ffn_small(H, I, E, k, n, hot):
         assert torch.equal(L.buffer_view(0, b).cpu(), hb.banks[b])
 
 
+def test_prefill_ffn_edges():
+    """n = 0 launches nothing; one token with one pair (a single row padded to a full
+    m-tile); skipped pairs (-1 and ids >= E) and a token with every pair skipped (y = 0)."""
+    H, I, E = 128, 192, 16
+    w = Workload(f"pf-edge-{H}-{I}-{E}", "mxfp4_t", L=1, E=E, k=2, H=H, I=I, S=0)
+    hb = make_host_banks(w)
+    L = _layers(w, hb)
+    L.prefetch(0)
+    dev = G.dev()
+    _case("prefill ffn n=0")
+    y0 = torch.full((0, H), 7, dtype=torch.int16, device=dev)
+    L.ffn(0, torch.empty((0, H), dtype=torch.int16, device=dev), torch.empty((0, 2), dtype=torch.int32, device=dev),
+          torch.empty((0, 2), dtype=torch.float32, device=dev), y0,
+          torch.empty(max(16, L.ffn_workspace_bytes(0, 2)), dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    rows = _oracle_rows(hb, None)
+    for n, k in ((1, 1), (40, 2)):
+        _case(f"prefill ffn edges n={n} k={k}")
+        logits = synth.router_logits(n, E, 1, w.name).numpy()
+        ids, wts = oroute.topk_softmax(logits, k)
+        ids = ids.astype(np.int32)
+        if n > 1:
+            ids[3, :] = -1           # every pair skipped
+            ids[4, 0] = E            # out of range: skipped
+            ids[5, 1] = 1 << 30
+        x = synth.activations(n, H, 1, w.name).to(dev)
+        y = _run_ffn(L, 0, x, torch.from_numpy(ids).to(dev), torch.from_numpy(wts.astype(np.float32)).to(dev))
+        torch.cuda.synchronize()
+        oids = np.where((ids >= 0) & (ids < E), ids, -1)
+        ref = offn.expert_ffn("mxfp4_t", H, I, G.bits16(x), oids, wts.astype(np.float32).astype(np.float64), rows)
+        got = G.bf16_tensor_to_f64(y)
+        if n > 1:
+            assert not got[3].any() and not ref[3].any()
+        err = offn.rel_l2(got, ref)
+        print(f"  rel_l2={err:.3e}")
+        assert err <= 4e-3
+
+
 def test_prefill_ffn_activation_ranges():
     """The two e4m3 activation planes across value ranges: a zero row, a constant row,
     rows whose 32-element blocks span 2^30 (beyond the 2^13 exact range), tiny and
