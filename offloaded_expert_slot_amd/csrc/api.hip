@@ -897,7 +897,7 @@ extern "C" oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t 
   a.slot_ids = slot_ids;
   a.w = w;
   a.y = static_cast<uint16_t *>(y);
-  a.h = static_cast<float *>(workspace);
+  a.h = static_cast<uint16_t *>(workspace);
   for (int b = 0; b < c->sc.num_banks; ++b) {
     a.bank[b] = c->slot_bank[b];
     a.row_bytes[b] = c->sc.bank[b].row_bytes;

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(KArgs ka) {
     g = tot;
     u = other;
     const float hv = g / (1.f + __expf(-g)) * u;
-    reinterpret_cast<uint16_t *>(a.h)[(int64_t)p * a.I + r] = f32_to_bf16_rne(hv);
+    a.h[(int64_t)p * a.I + r] = f32_to_bf16_rne(hv);
   }
 }
 
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int lrb) {
   const int ips = (items + NSG - 1) / NSG;
   const int i_end = min(items, (sg + 1) * ips);
   const Mat &m = ka.dn;
-  const uint16_t *hbase = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)t * k * a.I;
+  const uint16_t *hbase = a.h + (int64_t)t * k * a.I;
   const uint32_t row_bytes = (uint32_t)m.row_bytes;
   const uint32_t scale_ld = (uint32_t)m.scale_ld;
   u32x4 hreg[NQ][OPC];

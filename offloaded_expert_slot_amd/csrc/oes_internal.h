@@ -86,7 +86,7 @@ struct FfnArgs {
   const int32_t *slot_ids;
   const float *w;
   uint16_t *y;
-  float *h;                              // workspace [n*k, I]
+  uint16_t *h;                           // bf16 workspace [n*k, I]
   const uint8_t *bank[OES_MAX_BANKS];    // slot banks
   int64_t row_bytes[OES_MAX_BANKS];
   const int32_t *gate;                   // step_ok, or nullptr
