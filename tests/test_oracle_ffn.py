@@ -128,21 +128,46 @@ def test_q4_0_dequant_structure():
 
 @pytest.mark.parametrize("fmt,H,I", [("bf16", 32, 16), ("mxfp4_t", 64, 32)])
 def test_zero_input_closed_form(fmt, H, I):
+    """x = 0: y = sum_j w_j (b_d + Wd (silu(b_gate) * b_up)), which is 0 without biases.
+    The MXFP4 side is evaluated from a decoder written apart from the oracle (literal
+    OCP e2m1 table, torch's e8m0 type, torch's SiLU), in torch float64."""
+    import torch
+
+    from tests import mxfp4_torch_ref as ref
     experts = [synth.expert_rows(fmt, H, I, 0, "z", e) for e in range(2)]
     w = np.array([[0.7, 0.3]])
     xb = np.zeros((1, H), dtype=np.uint16)
     y = ffn.expert_ffn(fmt, H, I, xb, np.array([[0, 1]]), w, lambda s: _rows_np(experts[s]))
-    want = np.zeros(H)
-    for j in range(2):
-        wg, wd, bg, bd = ffn.dequant_expert(fmt, H, I, _rows_np(experts[j]))
-        if bg is not None:
-            g, u = bg[:I], bg[I:]
-            want += w[0, j] * (bd + wd @ (g / (1 + np.exp(-g)) * u))
     if fmt == "bf16":
         assert (y == 0).all()
-    else:
-        assert np.allclose(y, want, rtol=1e-12, atol=0)
-        assert np.abs(want).max() > 0
+        return
+    want = torch.zeros(H, dtype=torch.float64)
+    for j in range(2):
+        _, wd, bgu, bd = ref.expert(_rows_np(experts[j]), H, I)
+        want += w[0, j] * (bd + wd @ (torch.nn.functional.silu(bgu[:I]) * bgu[I:]))
+    assert np.allclose(y[0], want.numpy(), rtol=1e-12, atol=0)
+    assert want.abs().max() > 0
+
+
+def test_mxfp4_decoder_matches_independent_torch_decoder():
+    """The oracle's MXFP4 (transposed) dequant against the torch-float64 decoder on
+    seeded experts and on bytes covering every code and a spread of scales."""
+    from tests import mxfp4_torch_ref as ref
+    H, I = 64, 32
+    rows = _rows_np(synth.expert_rows("mxfp4_t", H, I, 0, "dq", 5))
+    wgu, wd, bgu, bd = ffn.dequant_expert("mxfp4_t", H, I, rows)
+    tg, td, tbg, tbd = ref.expert(rows, H, I)
+    assert np.array_equal(wgu, tg.numpy()) and np.array_equal(wd, td.numpy())
+    assert np.array_equal(bgu, tbg.numpy()) and np.array_equal(bd, tbd.numpy())
+    rng = np.random.default_rng(3)
+    raw = [r.copy() for r in rows]
+    raw[0] = rng.integers(0, 256, raw[0].size, dtype=np.uint8)         # every code
+    raw[1] = rng.integers(100, 155, raw[1].size, dtype=np.uint8)       # scales 2^-27 .. 2^27
+    raw[3] = rng.integers(0, 256, raw[3].size, dtype=np.uint8)
+    raw[4] = rng.integers(100, 155, raw[4].size, dtype=np.uint8)
+    wgu, wd, _, _ = ffn.dequant_expert("mxfp4_t", H, I, raw)
+    tg, td, _, _ = ref.expert(raw, H, I)
+    assert np.array_equal(wgu, tg.numpy()) and np.array_equal(wd, td.numpy())
 
 
 def test_slot_permutation_and_linearity():

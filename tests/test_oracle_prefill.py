@@ -1,15 +1,15 @@
 """Pins of the prefill oracle: the buffer is a byte copy of the layer, and the layer FFN
 is the routed expert FFN with slot = expert (FreeToken architecture walk-through §5)."""
 import numpy as np
+import torch
 
 import synth
-from oracle import ffn, prefill, route
+from oracle import prefill, route
+from tests import mxfp4_torch_ref as ref
 
 
 def test_prefill_layer_is_routed_ffn_on_buffer():
     fmt, H, I, E, k, n = "mxfp4_t", 64, 32, 6, 2, 5
-    specs_bytes = None
-    host = None
     rows = [synth.expert_rows(fmt, H, I, 0, "pf", e) for e in range(E)]
     nb = len(rows[0])
     host = [[np.concatenate([rows[e][b].numpy() for e in range(E)]).reshape(E, -1)] for b in range(nb)]
@@ -22,13 +22,13 @@ def test_prefill_layer_is_routed_ffn_on_buffer():
     ids, w, y = prefill.prefill_layer(fmt, H, I, xb, logits, k, buf)
     ids2, w2 = route.topk_softmax(logits, k)
     assert np.array_equal(ids, ids2) and np.array_equal(w, w2)
-    # the same FFN, one token at a time, expert by expert
+    # the same FFN, one token at a time, from an MXFP4 decoder written apart from the
+    # oracle (literal e2m1 table, torch e8m0, torch SiLU), in torch float64
+    x64 = torch.from_numpy(xb.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
     for t in range(n):
-        acc = np.zeros(H)
+        acc = torch.zeros(H, dtype=torch.float64)
         for j in range(k):
-            e = ids[t, j]
-            wg, wd, bg, bd = ffn.dequant_expert(fmt, H, I, [buf[b][e] for b in range(nb)])
-            x = ffn.decode.bf16(xb[t])
-            a = wg @ x + bg
-            acc += w[t, j] * (wd @ (ffn.silu(a[:I]) * a[I:]) + bd)
-        assert np.allclose(y[t], acc, rtol=1e-12, atol=1e-14)
+            e = int(ids[t, j])
+            acc += float(w[t, j]) * ref.output(x64[t:t + 1], [buf[b][e] for b in range(nb)], H, I)[0]
+        assert np.allclose(y[t], acc.numpy(), rtol=1e-12, atol=1e-14)
+    assert np.abs(y).max() > 0
