@@ -318,6 +318,23 @@ oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t *slot_ids, 
                           int32_t n, int32_t k, void *y, void *workspace, int64_t workspace_bytes,
                           void *stream);
 
+/* expert_ffn for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results as oes_expert_ffn, with the workspace taken from a
+ * library-owned device array of OES_FFN_NOALLOC_SCRATCH_BYTES per GPU (placed
+ * with the library's device code on each GPU it runs on, held until the
+ * process ends) instead of an argument.  Calls no hipMalloc / hipFree or other allocating routine.
+ * Requires oes_expert_ffn_workspace(c, n, k) <= OES_FFN_NOALLOC_SCRATCH_BYTES
+ * (2 * n * k * I bytes: n * k <= 2730 at I = 768, <= 1024 at I = 2048), else
+ * OES_ERR_ARG with a message naming both sizes and nothing enqueued.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, or two caches on two threads) race on it and are not allowed;
+ * calls ordered on one stream are fine (each call writes every workspace entry
+ * it later reads).  Other arguments and errors as oes_expert_ffn.  Async. */
+#define OES_FFN_NOALLOC_SCRATCH_BYTES (4 << 20)
+oes_status oes_expert_ffn_noalloc(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
+                                  int32_t n, int32_t k, void *y, void *stream);
+
 /* ------------------------------------------------------------------ prefill layer streaming */
 /*
  * Whole-layer double-buffered streaming for prefill (architecture walk-through

@@ -32,6 +32,7 @@ ELEM_BF16, ELEM_E4M3, ELEM_F32, ELEM_FP4X2, ELEM_FP16, ELEM_E8M0, ELEM_U8, ELEM_
 OPT_FUSED_COPY, OPT_COPY_MODE, OPT_COPY_BLOCKS = 1, 2, 3
 COPY_ZERO, COPY_SDMA = 0, 1
 OK, ERR_ARG, ERR_CAPACITY, ERR_HIP, ERR_NOMEM, ERR_STATE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+FFN_NOALLOC_SCRATCH_BYTES = 4 << 20   # OES_FFN_NOALLOC_SCRATCH_BYTES of include/oes.h
 MAX_BANKS = 6
 MAX_SLOTS = 4096
 
@@ -105,6 +106,7 @@ _SIGS = {
     "oes_copy_missing": (_I32, [_P, _P]),
     "oes_expert_ffn_workspace": (_I32, [_P, _I32, _I32, _PI64]),
     "oes_expert_ffn": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P, _I64, _P]),
+    "oes_expert_ffn_noalloc": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P]),
     "oes_layers_create": (_I32, [ctypes.POINTER(Schema), _I32, _I32, ctypes.POINTER(_P)]),
     "oes_layers_destroy": (_I32, [_P]),
     "oes_layers_set_source": (_I32, [_P, _I32, _I32, _P, _I64]),
@@ -341,6 +343,12 @@ class Cache:
         n, k = slot_ids.shape
         _check(lib().oes_expert_ffn(self._h, _ptr(x), _ptr(slot_ids), _ptr(w), n, k, _ptr(y), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+
+    def expert_ffn_noalloc(self, x, slot_ids, w, y, stream=None):
+        """expert_ffn on the library's own per-GPU scratch array (no workspace, no allocation)."""
+        n, k = slot_ids.shape
+        _check(lib().oes_expert_ffn_noalloc(self._h, _ptr(x), _ptr(slot_ids), _ptr(w), n, k, _ptr(y),
+                                            _stream(stream)))
 
 
 def route_workspace_bytes(n, hidden, num_experts):

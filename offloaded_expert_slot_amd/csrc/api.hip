@@ -870,21 +870,27 @@ extern "C" oes_status oes_expert_ffn_workspace(const oes_cache *c, int32_t n, in
   return OES_OK;
 }
 
-extern "C" oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
-                                     int32_t n, int32_t k, void *y, void *workspace, int64_t workspace_bytes,
-                                     void *stream) {
+// Checks of expert_ffn's arguments other than the workspace; *skip = true for n = 0.
+static oes_status ffn_check(const oes_cache *c, const void *x, const int32_t *slot_ids, const float *w, int32_t n,
+                            int32_t k, const void *y, bool *skip) {
+  *skip = false;
   if (!c) return fail(OES_ERR_ARG, "cache is NULL");
   if (n < 0 || k < 1 || k > 32) return fail(OES_ERR_ARG, "need n >= 0 and 1 <= k <= 32");
   if ((int64_t)n * k > 32768) return fail(OES_ERR_ARG, "n*k exceeds 32768");
-  if (n == 0) return OES_OK;
-  if (!x || !slot_ids || !w || !y || !workspace) return fail(OES_ERR_ARG, "NULL buffer");
-  int64_t need = 0;
-  oes_expert_ffn_workspace(c, n, k, &need);
-  if (workspace_bytes < need) return fail(OES_ERR_ARG, "workspace %lld < %lld bytes", (long long)workspace_bytes, (long long)need);
+  if (n == 0) {
+    *skip = true;
+    return OES_OK;
+  }
+  if (!x || !slot_ids || !w || !y) return fail(OES_ERR_ARG, "NULL buffer");
   if (!expert_ffn_supported(c->sc.format, c->sc.hidden, c->sc.inter, k))
     return fail(OES_ERR_UNSUPPORTED, "expert_ffn does not support format %d with H=%d I=%d k=%d", c->sc.format,
                 c->sc.hidden, c->sc.inter, k);
-  DeviceGuard g(c->device);
+  return OES_OK;
+}
+
+// Enqueues the FFN kernels with `workspace` (checked by the caller); the cache's device is current.
+static oes_status ffn_enqueue(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w, int32_t n,
+                              int32_t k, void *y, void *workspace, void *stream) {
   FfnArgs a;
   memset(&a, 0, sizeof(a));
   a.format = c->sc.format;
@@ -906,6 +912,37 @@ extern "C" oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t 
   a.err = &c->ctl->err;
   HIP_TRY(launch_expert_ffn(a, as_stream(stream)));
   return OES_OK;
+}
+
+extern "C" oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
+                                     int32_t n, int32_t k, void *y, void *workspace, int64_t workspace_bytes,
+                                     void *stream) {
+  bool skip = false;
+  oes_status st = ffn_check(c, x, slot_ids, w, n, k, y, &skip);
+  if (st != OES_OK || skip) return st;
+  if (!workspace) return fail(OES_ERR_ARG, "NULL buffer");
+  int64_t need = 0;
+  oes_expert_ffn_workspace(c, n, k, &need);
+  if (workspace_bytes < need) return fail(OES_ERR_ARG, "workspace %lld < %lld bytes", (long long)workspace_bytes, (long long)need);
+  DeviceGuard g(c->device);
+  return ffn_enqueue(c, x, slot_ids, w, n, k, y, workspace, stream);
+}
+
+extern "C" oes_status oes_expert_ffn_noalloc(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
+                                             int32_t n, int32_t k, void *y, void *stream) {
+  bool skip = false;
+  oes_status st = ffn_check(c, x, slot_ids, w, n, k, y, &skip);
+  if (st != OES_OK || skip) return st;
+  int64_t need = 0;
+  oes_expert_ffn_workspace(c, n, k, &need);
+  if (need > (int64_t)OES_FFN_NOALLOC_SCRATCH_BYTES)
+    return fail(OES_ERR_ARG, "expert_ffn_noalloc: n=%d k=%d needs %lld workspace bytes, more than the %lld-byte "
+                "scratch array (use oes_expert_ffn with a workspace)", n, k, (long long)need,
+                (long long)OES_FFN_NOALLOC_SCRATCH_BYTES);
+  DeviceGuard g(c->device);
+  void *ws = nullptr;
+  HIP_TRY(ffn_noalloc_scratch(c->device, &ws));
+  return ffn_enqueue(c, x, slot_ids, w, n, k, y, ws, stream);
 }
 
 // ============================================================================ prefill layers

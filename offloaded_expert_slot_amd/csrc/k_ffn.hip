@@ -27,6 +27,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "oes_internal.h"
 
@@ -668,6 +669,31 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t s) {
     case OES_Q4_0: return launch_fmt<OES_Q4_0>(ka, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ------------------------------------------------------------------ no-alloc scratch
+// Workspace of oes_expert_ffn_noalloc: one array per GPU, alive until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host the name
+// is only a stand-in); it passes the device address looked up here, once per
+// device with that device current.
+static __device__ __align__(256) uint8_t scratch[OES_FFN_NOALLOC_SCRATCH_BYTES];
+
+hipError_t ffn_noalloc_scratch(int device, void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  *ptr = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_debug_decode(int elem, const uint8_t *codes, int n, float *out, hipStream_t s) {

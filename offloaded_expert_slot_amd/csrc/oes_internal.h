@@ -94,6 +94,9 @@ struct FfnArgs {
 };
 // Returns hipErrorInvalidValue when the shape cannot be tiled (caller maps it to UNSUPPORTED).
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t s);
+// Device address of the file-scope FFN scratch array on the current device
+// (looked up once per device; nullptr and the HIP error on failure).
+hipError_t ffn_noalloc_scratch(int device, void **ptr);
 bool expert_ffn_supported(int format, int H, int I, int k);
 
 // ---------------------------------------------------------------- prefill grouped FFN (MXFP4)

@@ -65,6 +65,7 @@ def test_null_and_range_errors_without_gpu(L):
         (L.oes_copy_missing, (None, None)),
         (L.oes_ensure_experts, (None, 0, None, 1, 1, None, None)),
         (L.oes_expert_ffn, (None, None, None, None, 1, 1, None, None, 0, None)),
+        (L.oes_expert_ffn_noalloc, (None, None, None, None, 1, 1, None, None)),
         (L.oes_cache_check, (None, None)),
         (L.oes_layers_prefetch, (None, 0, None)),
         (L.oes_layers_ffn, (None, 0, None, None, None, 1, 1, None, None, 0, None)),
@@ -79,6 +80,13 @@ def test_null_and_range_errors_without_gpu(L):
     assert L.oes_route(None, None, 0, 64, 16, 2, None, None, None, None, 0, None) == oes.OK       # empty
     assert L.oes_route_logits(None, 2, 16, 2, None, None, None) == oes.ERR_ARG
     assert L.oes_debug_decode(oes.ELEM_U8, None, 4, None, None) == oes.ERR_ARG
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    import re
+    text = open(oes.HEADER_PATH).read()
+    m = re.search(r"#define OES_FFN_NOALLOC_SCRATCH_BYTES \((\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == oes.FFN_NOALLOC_SCRATCH_BYTES
 
 
 def test_header_lists_binding_functions():
