@@ -192,7 +192,9 @@ oes_status oes_cache_restore(oes_cache *c, void *stream);
 oes_status oes_cache_resize(oes_cache *c, int32_t num_slots, void *stream);
 
 /* Read the slot table into host arrays of num_slots entries (any pointer may
- * be NULL).  Syncs `stream`. */
+ * be NULL): the state the benchmark prepares and the LRU maintains (benchmark
+ * guide §4.3; architecture walk-through §5: the unified slot cache).  Syncs
+ * `stream`. */
 oes_status oes_cache_get_state(oes_cache *c, int64_t *owner, uint64_t *stamp, uint64_t *clock,
                                void *stream);
 
@@ -213,10 +215,15 @@ oes_status oes_cache_slot_bank(const oes_cache *c, int32_t bank, void **dev_base
 oes_status oes_cache_info(const oes_cache *c, int32_t *num_slots, oes_schema *schema);
 
 /* Miss list of the last ensure_experts: *count entries (slot, flat id) in
- * install order (ascending id).  Copies at most `cap` entries.  Syncs. */
+ * install order (ascending id), the list copy_missing consumes (benchmark
+ * guide §4.1, §4.4: ensure_experts yields the missing experts, copy_missing
+ * gathers them).  Copies at most `cap` entries.  Syncs. */
 oes_status oes_cache_get_misses(oes_cache *c, int32_t *count, int32_t *slots, int64_t *ids,
                                 int32_t cap, void *stream);
-/* Counters since creation.  Syncs. */
+/* Counters since creation (benchmark guide §4.3: hits and misses of the
+ * remap, bytes copied; §5.4: last_indices is num_indices, the misses fetched
+ * by the last step, and last_missing_full is num_missing_full, its misses
+ * before the hybrid cap).  Syncs. */
 oes_status oes_cache_stats(oes_cache *c, oes_stats *out, void *stream);
 /* Syncs `stream`, then returns and clears the sticky device error: OES_OK,
  * OES_ERR_CAPACITY (a step requested more distinct experts than slots) or
@@ -228,7 +235,9 @@ oes_status oes_cache_check(oes_cache *c, void *stream);
  * at creation).  OES_OPT_COPY_MODE: OES_COPY_ZERO (default) the gather
  * kernel reads mapped pinned memory; OES_COPY_SDMA copy_missing syncs the
  * stream, reads the miss list and issues one DMA copy per (miss, bank)
- * (default from env OES_COPY_MODE=zerocopy|sdma).  OES_OPT_COPY_BLOCKS: grid
+ * (default from env OES_COPY_MODE=zerocopy|sdma): the DMA engines need the
+ * rows' addresses on the host, so in this A/B mode copy_missing is not
+ * asynchronous - the one step call that waits for the GPU.  OES_OPT_COPY_BLOCKS: grid
  * size of the gather (0 = default). */
 enum { OES_OPT_FUSED_COPY = 1, OES_OPT_COPY_MODE = 2, OES_OPT_COPY_BLOCKS = 3 };
 enum { OES_COPY_ZERO = 0, OES_COPY_SDMA = 1 };
@@ -253,8 +262,11 @@ oes_status oes_route(const void *x, const void *wg, int32_t n, int32_t hidden,
                      int32_t num_experts, int32_t k, int32_t *ids, float *w, float *logits,
                      void *workspace, int64_t workspace_bytes, void *stream);
 
-/* Top-k of given router logits [n, E] float device (prefill routes given logits).
- * Limits: 1 <= E <= 512, 1 <= k <= min(E, 32). */
+/* Top-k of given router logits [n, E] float device: the same softmax, top-k
+ * and renormalisation as oes_route without the router matmul (the prefill
+ * layer routes its tokens' given logits before the grouped FFN of the
+ * streamed layer, architecture walk-through §5).  ids [n, k] int32, w [n, k]
+ * float, device.  Limits: 1 <= E <= 512, 1 <= k <= min(E, 32), n >= 0.  Async. */
 oes_status oes_route_logits(const float *logits, int32_t n, int32_t num_experts, int32_t k,
                             int32_t *ids, float *w, void *stream);
 
@@ -297,9 +309,10 @@ oes_status oes_ensure_experts_hybrid(oes_cache *c, int32_t layer, const int32_t 
 /* copy_missing: for every (slot, flat id) of the last miss list and every bank
  * b, copy row id % E of layer id / E's host bank b into slot row `slot` of
  * slot bank b (benchmark guide §4.1, §4.4: a per-bank index gather, fused
- * across banks in one launch).  Async (zero-copy mode).  A miss whose layer
- * has no registered source for some bank is skipped and sets OES_ERR_ARG in
- * the sticky status. */
+ * across banks in one launch).  Async in the default zero-copy mode; in the
+ * OES_COPY_SDMA mode it syncs `stream` first (see oes_cache_set_option).  A
+ * miss whose layer has no registered source for some bank is skipped and sets
+ * OES_ERR_ARG in the sticky status. */
 oes_status oes_copy_missing(oes_cache *c, void *stream);
 
 /* Workspace bytes expert_ffn needs for n tokens with top-k. */
