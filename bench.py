@@ -593,23 +593,32 @@ def _ffn_cold(w, cache, hb, host, sc, probes, log, launches=64):
             maps.append(sl)
         y = torch.empty((bs, w.H), dtype=torch.int16, device=dev)
         ws = torch.empty(cache.ffn_workspace_bytes(bs, w.k), dtype=torch.uint8, device=dev)
-        for i in range(4):
-            cache.expert_ffn(x, maps[i % R], wts, y, ws)
-        torch.cuda.synchronize()
-        cache.check()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        _hold_gpu(5.0)
-        a.record(stream)
-        for i in range(launches):
-            cache.expert_ffn(x, maps[i % R], wts, y, ws)
-        b.record(stream)
-        torch.cuda.synchronize()
-        cache.check()
-        ms = a.elapsed_time(b) / launches
+        def timed(path):
+            cache.set_option(oes.OPT_FFN_PATH, path)
+            for i in range(4):
+                cache.expert_ffn(x, maps[i % R], wts, y, ws)
+            torch.cuda.synchronize()
+            cache.check()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            _hold_gpu(5.0)
+            a.record(stream)
+            for i in range(launches):
+                cache.expert_ffn(x, maps[i % R], wts, y, ws)
+            b.record(stream)
+            torch.cuda.synchronize()
+            cache.check()
+            return a.elapsed_time(b) / launches
+
+        # several tokens: both FFN paths beside the default choice (run last, so that y
+        # below is the default path's)
+        paths = {}
+        if bs > 1:
+            paths = {"per_pair_ms": timed(oes.FFN_PER_PAIR), "grouped_ms": timed(oes.FFN_GROUPED)}
+        ms = timed(oes.FFN_AUTO)
         nbytes = u * bpe
         row = {"what": f"ffn bs={bs}", "bs": bs, "unique_experts": u, "bytes": nbytes, "avg_ms": ms,
                "GBps": nbytes / (ms * 1e6), "frac_of_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
-               "disjoint_sets": R, "launches": launches,
+               "disjoint_sets": R, "launches": launches, **paths,
                "traffic": _pmc_traffic(f"expert_ffn_{w.fmt}_bs{bs}" if bs > 1 else f"expert_ffn_{w.fmt}")}
         if probes:
             row["frac_of_measured_hbm_read"] = row["GBps"] / probes["hbm_read_GBps"]

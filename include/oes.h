@@ -238,9 +238,15 @@ oes_status oes_cache_check(oes_cache *c, void *stream);
  * (default from env OES_COPY_MODE=zerocopy|sdma): the DMA engines need the
  * rows' addresses on the host, so in this A/B mode copy_missing is not
  * asynchronous - the one step call that waits for the GPU.  OES_OPT_COPY_BLOCKS: grid
- * size of the gather (0 = default). */
-enum { OES_OPT_FUSED_COPY = 1, OES_OPT_COPY_MODE = 2, OES_OPT_COPY_BLOCKS = 3 };
+ * size of the gather (0 = default).  OES_OPT_FFN_PATH: how expert_ffn runs
+ * several tokens - OES_FFN_PER_PAIR one GEMV per (token, pair), OES_FFN_GROUPED
+ * pairs grouped by slot so that each expert's rows are read once per call and
+ * dotted with all its tokens, OES_FFN_AUTO (default) grouped when the repeats
+ * expected of uniform top-k routing save at least 128 MB of weight reads.  One
+ * token always takes the per-pair path.  The paths agree to within rounding. */
+enum { OES_OPT_FUSED_COPY = 1, OES_OPT_COPY_MODE = 2, OES_OPT_COPY_BLOCKS = 3, OES_OPT_FFN_PATH = 4 };
 enum { OES_COPY_ZERO = 0, OES_COPY_SDMA = 1 };
+enum { OES_FFN_AUTO = 0, OES_FFN_PER_PAIR = 1, OES_FFN_GROUPED = 2 };
 oes_status oes_cache_set_option(oes_cache *c, int32_t option, int64_t value);
 
 /* ------------------------------------------------------------------ the step */
@@ -338,13 +344,14 @@ oes_status oes_expert_ffn(oes_cache *c, const void *x, const int32_t *slot_ids, 
  * with the library's device code on each GPU it runs on, held until the
  * process ends) instead of an argument.  Calls no hipMalloc / hipFree or other allocating routine.
  * Requires oes_expert_ffn_workspace(c, n, k) <= OES_FFN_NOALLOC_SCRATCH_BYTES
- * (2 * n * k * I bytes: n * k <= 2730 at I = 768, <= 1024 at I = 2048), else
+ * (about 2 n k I bytes for one token and 2 n k I + 4 n k (H + 3) for several:
+ * n k <= 1720 at H = 2048, I = 768; n k <= 511 at H = 7168, I = 2048), else
  * OES_ERR_ARG with a message naming both sizes and nothing enqueued.  Every
  * call on one GPU shares that GPU's array: calls that overlap on one GPU (two
  * streams, or two caches on two threads) race on it and are not allowed;
  * calls ordered on one stream are fine (each call writes every workspace entry
  * it later reads).  Other arguments and errors as oes_expert_ffn.  Async. */
-#define OES_FFN_NOALLOC_SCRATCH_BYTES (4 << 20)
+#define OES_FFN_NOALLOC_SCRATCH_BYTES (16 << 20)
 oes_status oes_expert_ffn_noalloc(oes_cache *c, const void *x, const int32_t *slot_ids, const float *w,
                                   int32_t n, int32_t k, void *y, void *stream);
 

@@ -29,10 +29,11 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "oes.h")
 BF16, FP8_BLOCK128, NVFP4, MXFP4_T, Q4_0 = 0, 1, 2, 3, 4
 FORMAT_IDS = {"bf16": BF16, "fp8_block128": FP8_BLOCK128, "nvfp4": NVFP4, "mxfp4_t": MXFP4_T, "q4_0": Q4_0}
 ELEM_BF16, ELEM_E4M3, ELEM_F32, ELEM_FP4X2, ELEM_FP16, ELEM_E8M0, ELEM_U8, ELEM_Q4X2 = range(8)
-OPT_FUSED_COPY, OPT_COPY_MODE, OPT_COPY_BLOCKS = 1, 2, 3
+OPT_FUSED_COPY, OPT_COPY_MODE, OPT_COPY_BLOCKS, OPT_FFN_PATH = 1, 2, 3, 4
+FFN_AUTO, FFN_PER_PAIR, FFN_GROUPED = 0, 1, 2
 COPY_ZERO, COPY_SDMA = 0, 1
 OK, ERR_ARG, ERR_CAPACITY, ERR_HIP, ERR_NOMEM, ERR_STATE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-FFN_NOALLOC_SCRATCH_BYTES = 4 << 20   # OES_FFN_NOALLOC_SCRATCH_BYTES of include/oes.h
+FFN_NOALLOC_SCRATCH_BYTES = 16 << 20   # OES_FFN_NOALLOC_SCRATCH_BYTES of include/oes.h
 MAX_BANKS = 6
 MAX_SLOTS = 4096
 

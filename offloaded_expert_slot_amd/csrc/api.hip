@@ -159,7 +159,7 @@ struct oes_cache {
   uint8_t *staging = nullptr;
   int64_t staging_bytes = 0;
   hipEvent_t staging_done = nullptr;
-  int fused_copy = 1, copy_mode = OES_COPY_ZERO, copy_blocks = 0;
+  int fused_copy = 1, copy_mode = OES_COPY_ZERO, copy_blocks = 0, ffn_path = OES_FFN_AUTO;
   uint8_t *snap = nullptr;  // device snapshot: owner | stamp | clock
   bool has_snap = false;
   hipEvent_t hybrid_ev = nullptr;  // hybrid step: the step's ids have reached the host
@@ -354,6 +354,11 @@ extern "C" oes_status oes_cache_set_option(oes_cache *c, int32_t option, int64_t
     case OES_OPT_COPY_BLOCKS:
       if (value < 0 || value > 65536) return fail(OES_ERR_ARG, "copy blocks outside [0, 65536]");
       c->copy_blocks = (int)value;
+      return OES_OK;
+    case OES_OPT_FFN_PATH:
+      if (value != OES_FFN_AUTO && value != OES_FFN_PER_PAIR && value != OES_FFN_GROUPED)
+        return fail(OES_ERR_ARG, "bad FFN path");
+      c->ffn_path = (int)value;
       return OES_OK;
     default: return fail(OES_ERR_ARG, "unknown option %d", option);
   }
@@ -866,7 +871,7 @@ extern "C" oes_status oes_ensure_experts_hybrid(oes_cache *c, int32_t layer, con
 extern "C" oes_status oes_expert_ffn_workspace(const oes_cache *c, int32_t n, int32_t k, int64_t *bytes) {
   if (!c || !bytes) return fail(OES_ERR_ARG, "NULL argument");
   if (n < 0 || k < 1) return fail(OES_ERR_ARG, "need n >= 0 and k >= 1");
-  *bytes = round_up(2ll * n * k * c->sc.inter, 256);  // h rows, bf16
+  *bytes = expert_ffn_workspace_bytes(n, k, c->sc.hidden, c->sc.inter);
   return OES_OK;
 }
 
@@ -899,11 +904,13 @@ static oes_status ffn_enqueue(oes_cache *c, const void *x, const int32_t *slot_i
   a.n = n;
   a.k = k;
   a.S = c->S;
+  a.E = c->sc.num_experts;
+  a.path = c->ffn_path;
   a.x = static_cast<const uint16_t *>(x);
   a.slot_ids = slot_ids;
   a.w = w;
   a.y = static_cast<uint16_t *>(y);
-  a.h = static_cast<uint16_t *>(workspace);
+  expert_ffn_carve(a, workspace);
   for (int b = 0; b < c->sc.num_banks; ++b) {
     a.bank[b] = c->slot_bank[b];
     a.row_bytes[b] = c->sc.bank[b].row_bytes;

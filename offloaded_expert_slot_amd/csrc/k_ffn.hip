@@ -223,6 +223,32 @@ __device__ inline float dot_row(const RowRegs &R, const uint16_t *op, const floa
   return acc;
 }
 
+// Dot products of two rows' chunks (gate and up) with one bf16 operand vector
+// in LDS, chunk by chunk: each operand chunk is read once for both rows.
+// The weight registers are marked as redefined here (an empty asm), so that a
+// caller looping over tokens converts the codes per token instead of hoisting
+// every converted chunk out of its loop (which would hold four to eight times
+// the registers).
+template <int FMT, int G>
+__device__ inline void dot_rows2(RowRegs &A, RowRegs &B, const uint16_t *op, const float *opsum, int lg, int nq,
+                                 float &da, float &db) {
+  constexpr int EPC = Epc<FMT>::v;
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxQ; ++q) {
+    if (q < nq) {
+      if (FMT != OES_BF16) asm volatile("" : "+v"(A.w[q]), "+v"(B.w[q]));
+      const int c = q * G + lg;
+      const float xs = FMT == OES_Q4_0 ? opsum[c] : 0.f;
+      const u32x4 *xo = reinterpret_cast<const u32x4 *>(op + c * EPC);
+      a += dot_chunk<FMT>(A.w[q], A.sc[q], xo, xs);
+      b += dot_chunk<FMT>(B.w[q], B.sc[q], xo, xs);
+    }
+  }
+  da = a;
+  db = b;
+}
+
 template <int G>
 __device__ inline float group_sum(float v) {
 #pragma unroll
@@ -459,6 +485,282 @@ __global__ __launch_bounds__(kThreads) void down_kernel(KArgs ka, int lrb) {
   }
 }
 
+// ------------------------------------------------------------------ grouped path (n >= 2)
+// With several tokens, pairs routed to the same slot share that expert's rows:
+// the rows are streamed once per step and dotted with every such pair's operand,
+// so the weight bytes read are u * bytes_per_expert (u = distinct slots) rather
+// than one expert per pair.
+//   group_pairs  - one workgroup: the distinct slots in ascending order, the
+//                  pairs of each (grp), from slot_ids.
+//   gate_up      - persistent blocks over (group, 256 / G rows): the group's
+//                  tokens' x rows staged in LDS (up to kMG per pass), each
+//                  subgroup's gate and up rows read once and dotted with all
+//                  of them; h per pair as before.
+//   down         - persistent blocks over (group, RB rows): the group's h rows
+//                  staged in LDS, each row read once; o per (pair, row) in fp32.
+//   combine      - y_t = sum_j w[t, j] * o_tj in pair order, bf16.
+// Every pair's dot products have the same reduction order whatever the group
+// sizes, so the results do not depend on the order of pairs inside a group.
+constexpr int kMG = 8;                   // pairs per LDS pass
+constexpr int kGroupThreads = 1024;
+constexpr int kSlotsPerThread = OES_MAX_SLOTS / kGroupThreads;
+
+struct GroupView {
+  int32_t *count, *slot, *start, *pairs;
+};
+__device__ inline GroupView group_view(const FfnArgs &a) {
+  const int nk = a.n * a.k;
+  return {a.grp, a.grp + 4, a.grp + 4 + nk, a.grp + 4 + 2 * nk + 1};
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_pairs_kernel(FfnArgs a) {
+  __shared__ int cnt[OES_MAX_SLOTS];   // pairs per slot, then each slot's scatter cursor
+  __shared__ int wsum[2][kGroupThreads / 64];
+  const GroupView gv = group_view(a);
+  const int nk = a.n * a.k, S = a.S;
+  if (a.gate && *a.gate == 0) {
+    if (threadIdx.x == 0) *gv.count = 0;
+    return;
+  }
+  for (int s = threadIdx.x; s < OES_MAX_SLOTS; s += kGroupThreads) cnt[s] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < nk; p += kGroupThreads) {
+    const int s = a.slot_ids[p];
+    if (s >= S)
+      atomicCAS(a.err, 0, (int)OES_ERR_ARG);
+    else if (s >= 0)
+      atomicAdd(&cnt[s], 1);
+  }
+  __syncthreads();
+  // thread i owns slots [4i, 4i + 4): exclusive scans, in slot order, of the
+  // group flags (count > 0) and of the counts
+  int c[kSlotsPerThread], f = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    c[j] = cnt[kSlotsPerThread * threadIdx.x + j];
+    f += c[j] > 0;
+    tot += c[j];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int fi = f, ti = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int fu = __shfl_up(fi, d), tu = __shfl_up(ti, d);
+    if (lane >= d) {
+      fi += fu;
+      ti += tu;
+    }
+  }
+  if (lane == 63) {
+    wsum[0][wave] = fi;
+    wsum[1][wave] = ti;
+  }
+  __syncthreads();
+  int fo = fi - f, to = ti - tot;
+  for (int w = 0; w < wave; ++w) {
+    fo += wsum[0][w];
+    to += wsum[1][w];
+  }
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    if (c[j] > 0) {
+      const int s = kSlotsPerThread * threadIdx.x + j;
+      gv.slot[fo] = s;
+      gv.start[fo] = to;
+      cnt[s] = to;
+      ++fo;
+      to += c[j];
+    }
+  }
+  if (threadIdx.x == kGroupThreads - 1) {  // its running sums end at the totals
+    *gv.count = fo;
+    gv.start[fo] = to;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < nk; p += kGroupThreads) {
+    const int s = a.slot_ids[p];
+    if (s >= 0 && s < S) gv.pairs[atomicAdd(&cnt[s], 1)] = p;
+  }
+}
+
+// Stages `mg` rows of `len` bf16 values into LDS (row i from src + rowidx(i) * len)
+// and, for q4_0, each row's per-32-element sums after them.
+template <int FMT, typename RowOf>
+__device__ inline void stage_rows(uint16_t *dst, float *sums, const uint16_t *src, int len, int mg, RowOf rowof) {
+  const int v = len / 8;
+  for (int i = 0; i < mg; ++i) {
+    const u32x4 *s = reinterpret_cast<const u32x4 *>(src + (int64_t)rowof(i) * len);
+    u32x4 *d = reinterpret_cast<u32x4 *>(dst + i * len);
+    for (int j = threadIdx.x; j < v; j += kThreads) d[j] = s[j];
+  }
+  if (FMT == OES_Q4_0) {
+    __syncthreads();
+    const int nb = len / 32;
+    for (int b = threadIdx.x; b < mg * nb; b += kThreads) {
+      const u32x4 *xv = reinterpret_cast<const u32x4 *>(dst) + 4 * b;  // rows are whole blocks
+      float acc = 0.f;
+#pragma unroll
+      for (int o = 0; o < 4; ++o) acc = sum8_bf16(xv[o], acc);
+      sums[b] = acc;
+    }
+  }
+}
+
+template <int FMT, int G>
+__global__ __launch_bounds__(kThreads) void gate_up_grouped_kernel(KArgs ka, int mgmax) {
+  extern __shared__ __align__(16) uint16_t xs[];  // mgmax x rows of H, then q4_0 block sums
+  __shared__ int sp[kMG];
+  const FfnArgs &a = ka.f;
+  if (a.gate && *a.gate == 0) return;
+  const GroupView gv = group_view(a);
+  const int ng = *gv.count;
+  constexpr int NSG = kThreads / G;
+  const int rblk = (a.I + NSG - 1) / NSG;
+  const int sg = threadIdx.x / G, lg = threadIdx.x % G;
+  float *xsums = reinterpret_cast<float *>(xs + (size_t)mgmax * a.H);
+  const int nb = a.H / 32;
+  const Mat &m = ka.gu;
+  const int nqt = m.C / G;  // chunks per lane of a row
+  for (int item = blockIdx.x; item < ng * rblk; item += gridDim.x) {
+    const int g = item / rblk;
+    const int r = (item - g * rblk) * NSG + sg;
+    const int slot = gv.slot[g], p0 = gv.start[g], p1 = gv.start[g + 1];
+    for (int pp = p0; pp < p1; pp += mgmax) {
+      const int mg = min(mgmax, p1 - pp);
+      __syncthreads();  // the previous pass is done with xs and sp
+      if ((int)threadIdx.x < mg) sp[threadIdx.x] = gv.pairs[pp + threadIdx.x];
+      __syncthreads();
+      stage_rows<FMT>(xs, xsums, a.x, a.H, mg, [&](int i) { return sp[i] / a.k; });
+      __syncthreads();
+      if (r < a.I) {
+        // the rows stay in registers (one pass: C / G <= kMaxQ, checked at launch)
+        // while every staged token is dotted with them
+        RowRegs Rg, Ru;
+        load_row<FMT, G>(Rg, m, slot, r, lg, 0, nqt);
+        load_row<FMT, G>(Ru, m, slot, a.I + r, lg, 0, nqt);
+#pragma unroll 1
+        for (int i = 0; i < mg; ++i) {
+          float dg, du;
+          dot_rows2<FMT, G>(Rg, Ru, xs + i * a.H, xsums + i * nb, lg, nqt, dg, du);
+          float gu2[2] = {dg * Rg.gl, du * Ru.gl};
+          const float tot = group_sum_multi<G, 2>(gu2, lg);  // lanes [0, G/2): gate, [G/2, G): up
+          const float other = __shfl_xor(tot, G / 2, G);
+          if (lg == 0) a.h[(int64_t)sp[i] * a.I + r] = f32_to_bf16_rne(tot / (1.f + __expf(-tot)) * other);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int G, int NQ>
+__global__ __launch_bounds__(kThreads) void down_grouped_kernel(KArgs ka, int mgmax) {
+  extern __shared__ __align__(16) uint16_t hs[];  // mgmax h rows of I, then q4_0 block sums
+  __shared__ int sp[kMG];
+  constexpr int EPC = Epc<FMT>::v;
+  constexpr int IB = 4;                 // consecutive rows per subgroup
+  constexpr int NSG = kThreads / G;
+  constexpr int RB = NSG * IB;          // rows per work item
+  const FfnArgs &a = ka.f;
+  if (a.gate && *a.gate == 0) return;
+  const GroupView gv = group_view(a);
+  const int ng = *gv.count;
+  const int rblk = (a.H + RB - 1) / RB;
+  const int sg = threadIdx.x / G, lg = threadIdx.x % G;
+  float *hsums = reinterpret_cast<float *>(hs + (size_t)mgmax * a.I);
+  const int nb = a.I / 32;
+  const Mat &m = ka.dn;
+  const uint32_t row_bytes = (uint32_t)m.row_bytes, scale_ld = (uint32_t)m.scale_ld;
+  for (int item = blockIdx.x; item < ng * rblk; item += gridDim.x) {
+    const int g = item / rblk;
+    const int row0 = (item - g * rblk) * RB + sg * IB;
+    const int slot = gv.slot[g], p0 = gv.start[g], p1 = gv.start[g + 1];
+    const uint8_t *cb = m.codes + (int64_t)slot * m.codes_slot;
+    const uint8_t *sb = FMT == OES_BF16 ? nullptr : m.scale + (int64_t)slot * m.scale_slot;
+    const uint16_t *gb =
+        FMT == OES_NVFP4 ? reinterpret_cast<const uint16_t *>(m.glob + (int64_t)slot * m.glob_slot) : nullptr;
+    for (int pp = p0; pp < p1; pp += mgmax) {
+      const int mg = min(mgmax, p1 - pp);
+      __syncthreads();
+      if ((int)threadIdx.x < mg) sp[threadIdx.x] = gv.pairs[pp + threadIdx.x];
+      __syncthreads();
+      // the rows' weights are loaded before the staging waits, so the two overlap
+      u32x4 w[IB][NQ];
+      uint32_t sc[IB][NQ];
+      float gl[IB];
+#pragma unroll
+      for (int b = 0; b < IB; ++b) {
+        const int row = min(row0 + b, a.H - 1);  // rows past H repeat the last row; never stored
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(cb + (uint32_t)row * row_bytes);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int c = q * G + lg;
+          w[b][q] = __builtin_nontemporal_load(p + c);
+          if (FMT == OES_FP8_BLOCK128)
+            sc[b][q] = reinterpret_cast<const uint32_t *>(sb)[(uint32_t)(row >> 7) * scale_ld + (c >> 3)];
+          else if (FMT == OES_NVFP4 || FMT == OES_Q4_0)
+            sc[b][q] = reinterpret_cast<const uint16_t *>(sb + (uint32_t)row * scale_ld)[c];
+          else
+            sc[b][q] = 0;
+        }
+        gl[b] = FMT == OES_NVFP4 ? fp16_to_f32(gb[row]) : 1.f;
+      }
+      stage_rows<FMT>(hs, hsums, a.h, a.I, mg, [&](int i) { return sp[i]; });
+      __syncthreads();
+#pragma unroll 1
+      for (int i = 0; i < mg; ++i) {
+        {
+          const uint16_t *hv = hs + i * a.I;
+          float acc[IB];
+#pragma unroll
+          for (int b = 0; b < IB; ++b) acc[b] = 0.f;
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {  // each h chunk is read once for all the rows
+            if (FMT != OES_BF16) {   // converted per token, not hoisted out of the token loop
+#pragma unroll
+              for (int b = 0; b < IB; ++b) asm volatile("" : "+v"(w[b][q]));
+            }
+            const int c = q * G + lg;
+            const u32x4 *ho = reinterpret_cast<const u32x4 *>(hv + c * EPC);
+            const float hsum = FMT == OES_Q4_0 ? hsums[i * nb + c] : 0.f;
+#pragma unroll
+            for (int b = 0; b < IB; ++b) acc[b] += dot_chunk<FMT>(w[b][q], sc[b][q], ho, hsum);
+          }
+#pragma unroll
+          for (int b = 0; b < IB; ++b) acc[b] *= gl[b];
+          const float v = group_sum_multi<G, IB>(acc, lg);  // row lg / (G / IB)
+          const int b = lg / (G / IB);
+          if (lg % (G / IB) == 0 && row0 + b < a.H) a.o[(int64_t)sp[i] * a.H + row0 + b] = v;
+        }
+      }
+    }
+  }
+}
+
+// y[t, c..c+3] = sum_j w[t, j] * o[t k + j, c..c+3] over the pairs with a slot, in j order.
+__global__ __launch_bounds__(256) void combine_pairs_kernel(FfnArgs a) {
+  if (a.gate && *a.gate == 0) return;
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= a.H) return;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    const int p = t * a.k + j;
+    const int slot = a.slot_ids[p];
+    if (slot < 0 || slot >= a.S) continue;
+    const float wt = a.w[p];
+    const float4 o = *reinterpret_cast<const float4 *>(a.o + (int64_t)p * a.H + c);
+    s0 = fmaf(wt, o.x, s0);
+    s1 = fmaf(wt, o.y, s1);
+    s2 = fmaf(wt, o.z, s2);
+    s3 = fmaf(wt, o.w, s3);
+  }
+  uint16_t *yr = a.y + (int64_t)t * a.H + c;
+  yr[0] = f32_to_bf16_rne(s0);
+  yr[1] = f32_to_bf16_rne(s1);
+  yr[2] = f32_to_bf16_rne(s2);
+  yr[3] = f32_to_bf16_rne(s3);
+}
+
 // ------------------------------------------------------------------ dispatch
 int pick_group(int C) {
   if (C % 64 == 0) return 64;
@@ -577,8 +879,118 @@ hipError_t launch_down_g(const KArgs &ka, hipStream_t s) {
   }
 }
 
+// ------------------------------------------------------------------ grouped dispatch
+// down subgroups of the grouped path: the widest G whose share of a row is at
+// most 4 chunks per lane.
+int pick_group_dn_grouped(int C) {
+  for (int g = 64; g >= 8; g /= 2)
+    if (C % g == 0 && C / g <= 4) return g;
+  return 0;
+}
+
+// Pairs per LDS pass: at most kMG, and at most 32 KiB of staged bf16 rows.
+int group_mg(int len) { return std::max(1, std::min(kMG, 32768 / (2 * len))); }
+
+size_t staged_lds(int fmt, int mg, int len) {
+  return (size_t)mg * len * 2 + (fmt == OES_Q4_0 ? (size_t)mg * (len / 32) * 4 : 0);
+}
+
+// Persistent grid: every CU holds as many blocks as fit, capped by the work items.
+template <typename K>
+int persistent_blocks(K kernel, size_t lds, int64_t items) {
+  int dev = 0, cus = 0, per_cu = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  (void)hipGetLastError();
+  return (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)cus * per_cu));
+}
+
+template <int FMT, int G>
+hipError_t launch_gate_up_grouped(const KArgs &ka, hipStream_t s) {
+  const FfnArgs &a = ka.f;
+  constexpr int NSG = kThreads / G;
+  const int mg = group_mg(a.H);
+  const size_t lds = staged_lds(FMT, mg, a.H);
+  const int64_t items = (int64_t)a.n * a.k * ((a.I + NSG - 1) / NSG);  // distinct slots <= pairs
+  auto kern = gate_up_grouped_kernel<FMT, G>;
+  hipLaunchKernelGGL(kern, dim3(persistent_blocks(kern, lds, items)), dim3(kThreads), lds, s, ka, mg);
+  return hipGetLastError();
+}
+
+template <int FMT, int G, int NQ>
+hipError_t launch_down_grouped_gq(const KArgs &ka, hipStream_t s) {
+  const FfnArgs &a = ka.f;
+  constexpr int RB = (kThreads / G) * 4;
+  const int mg = group_mg(a.I);
+  const size_t lds = staged_lds(FMT, mg, a.I);
+  const int64_t items = (int64_t)a.n * a.k * ((a.H + RB - 1) / RB);
+  auto kern = down_grouped_kernel<FMT, G, NQ>;
+  hipLaunchKernelGGL(kern, dim3(persistent_blocks(kern, lds, items)), dim3(kThreads), lds, s, ka, mg);
+  return hipGetLastError();
+}
+
+template <int FMT, int G>
+hipError_t launch_down_grouped_g(const KArgs &ka, hipStream_t s) {
+  switch (ka.dn.C / G) {
+    case 1: return launch_down_grouped_gq<FMT, G, 1>(ka, s);
+    case 2: return launch_down_grouped_gq<FMT, G, 2>(ka, s);
+    case 3: return launch_down_grouped_gq<FMT, G, 3>(ka, s);
+    case 4: return launch_down_grouped_gq<FMT, G, 4>(ka, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int FMT>
+hipError_t launch_fmt_grouped(const KArgs &ka, hipStream_t s) {
+  const FfnArgs &a = ka.f;
+  hipLaunchKernelGGL(group_pairs_kernel, dim3(1), dim3(kGroupThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (pick_group_gu(ka.gu.C, a.I, a.n * a.k)) {
+    case 64: e = launch_gate_up_grouped<FMT, 64>(ka, s); break;
+    case 32: e = launch_gate_up_grouped<FMT, 32>(ka, s); break;
+    case 16: e = launch_gate_up_grouped<FMT, 16>(ka, s); break;
+    case 8: e = launch_gate_up_grouped<FMT, 8>(ka, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  switch (pick_group_dn_grouped(ka.dn.C)) {
+    case 64: e = launch_down_grouped_g<FMT, 64>(ka, s); break;
+    case 32: e = launch_down_grouped_g<FMT, 32>(ka, s); break;
+    case 16: e = launch_down_grouped_g<FMT, 16>(ka, s); break;
+    case 8: e = launch_down_grouped_g<FMT, 8>(ka, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_pairs_kernel, dim3((a.H / 4 + 255) / 256, a.n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// The grouped path costs two more launches and the o round trip; it pays when
+// experts repeat enough.  The repeats expected of uniform top-k routing over E
+// experts, n k - E (1 - (1 - k / E)^n), must save at least 128 MB of weight reads
+// (measured on the decode workloads: bf16 H=2048 at 32 tokens 346 -> 180 us and
+// fp8 H=4096 at 16 tokens 356 -> 324 us grouped; nvfp4 H=7168 at 4 tokens, Q4_0
+// H=2048 at 8 and bf16 H=2048 at 8 no faster or slower), and a subgroup must hold
+// a whole gate / up row in registers.
+bool use_grouped(const KArgs &ka) {
+  const FfnArgs &a = ka.f;
+  if (a.n < 2 || a.path == OES_FFN_PER_PAIR) return false;
+  if (ka.gu.C > 64 * kMaxQ || ka.gu.C / pick_group_gu(ka.gu.C, a.I, a.n * a.k) > kMaxQ) return false;
+  if (a.path == OES_FFN_GROUPED) return true;
+  if (a.E <= 0) return false;
+  const double E = a.E, nk = (double)a.n * a.k;
+  const double unique = E * (1.0 - pow(1.0 - std::min(1.0, a.k / E), (double)a.n));
+  int64_t bpe = 0;
+  for (int b = 0; b < OES_MAX_BANKS; ++b) bpe += a.row_bytes[b];
+  return (nk - unique) * (double)bpe >= 128.0 * (1 << 20);
+}
+
 template <int FMT>
 hipError_t launch_fmt(const KArgs &ka, hipStream_t s) {
+  if (use_grouped(ka)) return launch_fmt_grouped<FMT>(ka, s);
   hipError_t e;
   switch (pick_group_gu(ka.gu.C, ka.f.I, ka.f.n * ka.f.k)) {
     case 64: e = launch_gate_up_g<FMT, 64>(ka, s); break;
@@ -651,10 +1063,37 @@ bool expert_ffn_supported(int format, int H, int I, int k) {
   if (!epc) return false;
   if (H % epc || I % epc) return false;
   const int gu = pick_group_gu(H / epc, I, k), dn = pick_group_dn(I / epc, k);
-  if (!gu || !dn) return false;  // down: at most 4 chunks per lane held in registers
+  if (!gu || !dn || !pick_group_dn_grouped(I / epc)) return false;  // down: at most 4 chunks per lane in registers
+  if (H % 4) return false;  // combine: four columns per thread
   if (H > 16384) return false;          // x row staged in LDS by gate_up
   if (k > 32 || 16 * k > kMaxRed) return false;
   return true;
+}
+
+// Workspace: h bf16 [n k, I]; for n >= 2 also o fp32 [n k, H] and the grouping
+// (count, then slot [n k], start [n k + 1], pairs [n k] as int32), each part
+// 256-byte aligned.
+static int64_t ws_round(int64_t v) { return (v + 255) / 256 * 256; }
+
+int64_t expert_ffn_workspace_bytes(int n, int k, int H, int I) {
+  const int64_t nk = (int64_t)n * k;
+  int64_t bytes = ws_round(2 * nk * I);
+  if (n >= 2) bytes += ws_round(4 * nk * H) + ws_round(4 * (4 + 3 * nk + 1));
+  return bytes;
+}
+
+void expert_ffn_carve(FfnArgs &a, void *workspace) {
+  uint8_t *p = static_cast<uint8_t *>(workspace);
+  const int64_t nk = (int64_t)a.n * a.k;
+  a.h = reinterpret_cast<uint16_t *>(p);
+  p += ws_round(2 * nk * a.I);
+  a.o = nullptr;
+  a.grp = nullptr;
+  if (a.n >= 2) {
+    a.o = reinterpret_cast<float *>(p);
+    p += ws_round(4 * nk * a.H);
+    a.grp = reinterpret_cast<int32_t *>(p);
+  }
 }
 
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t s) {

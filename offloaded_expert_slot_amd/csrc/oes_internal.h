@@ -82,16 +82,23 @@ hipError_t launch_route_logits(const float *logits, int n, int E, int k, int32_t
 struct FfnArgs {
   int32_t format;
   int32_t H, I, n, k, S;
+  int32_t E;                             // experts per layer (chooses the grouped path)
+  int32_t path;                          // OES_FFN_AUTO / OES_FFN_PER_PAIR / OES_FFN_GROUPED
   const uint16_t *x;
   const int32_t *slot_ids;
   const float *w;
   uint16_t *y;
-  uint16_t *h;                           // bf16 workspace [n*k, I]
+  uint16_t *h;                           // workspace: bf16 h rows [n*k, I]
+  float *o;                              // n >= 2: each pair's down output [n*k, H] (fp32)
+  int32_t *grp;                          // n >= 2: pairs grouped by slot (count, slots, starts, pairs)
   const uint8_t *bank[OES_MAX_BANKS];    // slot banks
   int64_t row_bytes[OES_MAX_BANKS];
   const int32_t *gate;                   // step_ok, or nullptr
   int32_t *err;
 };
+// Workspace bytes of the decode FFN for n tokens with top-k, and its carving into h / o / grp.
+int64_t expert_ffn_workspace_bytes(int n, int k, int H, int I);
+void expert_ffn_carve(FfnArgs &a, void *workspace);
 // Returns hipErrorInvalidValue when the shape cannot be tiled (caller maps it to UNSUPPORTED).
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t s);
 // Device address of the file-scope FFN scratch array on the current device

@@ -59,6 +59,7 @@ def _setup(name):
         _STATE[name] = dict(w=w, hb=hb, c=c, sc=sc)
     st = _STATE[name]
     st["c"].set_option(oes.OPT_FUSED_COPY, 1)
+    st["c"].set_option(oes.OPT_FFN_PATH, oes.FFN_AUTO)
     return st["w"], st["hb"], st["c"]
 
 
@@ -169,13 +170,15 @@ def test_decode_step(name, bs, mr):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("path", ["per_pair", "grouped"])
 @pytest.mark.parametrize("name,bs", [("bf16_h2048", 8), ("bf16_h2048", 32), ("fp8_h4096", 16),
                                      ("nvfp4_h7168", 4), ("q4_0_h2048", 8)])
-def test_decode_ffn_batched(name, bs):
+def test_decode_ffn_batched(name, bs, path):
     """Batched FFN on routed ids (every slot foreign, so every routed expert is
-    copied in first); the oracle checks every token."""
+    copied in first), on both FFN paths; the oracle checks every token."""
     w, hb, c = _setup(name)
-    _case(f"ffn {name} bs={bs}")
+    _case(f"ffn {name} bs={bs} path={path}")
+    c.set_option(oes.OPT_FFN_PATH, oes.FFN_GROUPED if path == "grouped" else oes.FFN_PER_PAIR)
     dev = G.dev()
     x = synth.activations(bs, w.H, 0, w.name, step=7).to(dev)
     wg = synth.router_weight(w.H, w.E, 0, w.name).to(dev)

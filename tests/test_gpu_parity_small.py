@@ -443,12 +443,16 @@ FFN_CASES += [
 ]
 
 
+@pytest.mark.parametrize("path", ["per_pair", "grouped"])
 @pytest.mark.parametrize("fmt,H,I,E,k,n", FFN_CASES)
-def test_expert_ffn_matches_oracle(fmt, H, I, E, k, n):
-    _case(f"ffn fmt={fmt} H={H} I={I} E={E} k={k} n={n}")
+def test_expert_ffn_matches_oracle(fmt, H, I, E, k, n, path):
+    if n == 1 and path == "grouped":
+        pytest.skip("one token always takes the per-pair path")
+    _case(f"ffn fmt={fmt} H={H} I={I} E={E} k={k} n={n} path={path}")
     S = E
     banks = {0: G.make_banks(fmt, E, H, I, tag=f"ffn-{fmt}-{H}")}
     c = G.make_cache(fmt, 1, E, H, I, S, banks)
+    c.set_option(oes.OPT_FFN_PATH, oes.FFN_GROUPED if path == "grouped" else oes.FFN_PER_PAIR)
     host = G.oracle_host(banks, 1, len(banks[0].banks))
     # slot s holds expert (s * 5 + 1) % E
     perm = [(s * 5 + 1) % E for s in range(S)] if E % 5 else list(reversed(range(E)))

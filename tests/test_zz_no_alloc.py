@@ -20,16 +20,18 @@ def _case(msg):
     print(f"[case] {msg}", flush=True)
 
 
+@pytest.mark.parametrize("path", ["per_pair", "grouped"])
 @pytest.mark.parametrize("fmt,H,I,E,k", [("bf16", 256, 128, 16, 2), ("fp8_block128", 1024, 512, 16, 4),
                                          ("nvfp4", 512, 256, 16, 4), ("q4_0", 512, 256, 16, 8)])
-def test_noalloc_matches_workspace_entry_point(fmt, H, I, E, k):
+def test_noalloc_matches_workspace_entry_point(fmt, H, I, E, k, path):
     dev = G.dev()
     hb = G.make_banks(fmt, E, H, I, tag=f"na-{fmt}")
     S = E
     c = G.make_cache(fmt, 1, E, H, I, S, {0: hb})
+    c.set_option(oes.OPT_FFN_PATH, oes.FFN_GROUPED if path == "grouped" else oes.FFN_PER_PAIR)
     owner, stamp, clock = synth.foreign_state(S, E)
     for n in (16, 3):   # the second call is smaller
-        _case(f"noalloc {fmt} H={H} I={I} E={E} k={k} n={n}")
+        _case(f"noalloc {fmt} H={H} I={I} E={E} k={k} n={n} path={path}")
         c.set_state(owner, stamp, clock)
         rng = np.random.default_rng(n)
         ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(n)]).astype(np.int32)
@@ -62,23 +64,47 @@ def test_noalloc_matches_workspace_entry_point(fmt, H, I, E, k):
     c.close()
 
 
-def test_noalloc_rejects_sizes_beyond_the_array():
+def _largest_n(c, k):
+    """The most tokens whose workspace fits the scratch array (host-side sizes only)."""
+    lo, hi = 1, 32768 // k
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if c.ffn_workspace_bytes(mid, k) <= oes.FFN_NOALLOC_SCRATCH_BYTES:
+            lo = mid
+        else:
+            hi = mid - 1
+    return lo
+
+
+def test_noalloc_at_the_limit_and_beyond():
+    """The largest call the array holds matches the workspace entry point; one token
+    more is refused before any GPU work."""
     dev = G.dev()
     fmt, H, I, E, k = "bf16", 256, 128, 16, 2
     hb = G.make_banks(fmt, E, H, I, tag="na-limit")
     c = G.make_cache(fmt, 1, E, H, I, E, {0: hb})
-    n = oes.FFN_NOALLOC_SCRATCH_BYTES // (2 * k * I) + 1      # one token more than the array holds
-    _case(f"noalloc limit n={n}")
-    assert c.ffn_workspace_bytes(n, k) > oes.FFN_NOALLOC_SCRATCH_BYTES
-    x = torch.zeros((n, H), dtype=torch.int16, device=dev)
-    slot_ids = torch.zeros((n, k), dtype=torch.int32, device=dev)
-    w = torch.zeros((n, k), dtype=torch.float32, device=dev)
+    c.set_option(oes.OPT_FFN_PATH, oes.FFN_GROUPED)    # the larger workspace of the two paths
+    c.load_rows(list(range(E)), list(range(E)))
+    n_ok = _largest_n(c, k)
+    n = n_ok + 1
+    _case(f"noalloc limit n_ok={n_ok}")
+    assert c.ffn_workspace_bytes(n_ok, k) <= oes.FFN_NOALLOC_SCRATCH_BYTES < c.ffn_workspace_bytes(n, k)
+    rng = np.random.default_rng(2)
+    slot_ids = torch.from_numpy(rng.integers(0, E, size=(n, k)).astype(np.int32)).to(dev)
+    w = torch.full((n, k), 0.5, dtype=torch.float32, device=dev)
+    x = synth.activations(n, H, 0, "na-limit").to(dev)
     y = torch.full((n, H), 7, dtype=torch.int16, device=dev)
     with pytest.raises(oes.OesError) as ei:
         c.expert_ffn_noalloc(x, slot_ids, w, y)
     assert ei.value.status == oes.ERR_ARG and "scratch" in str(ei.value)
     torch.cuda.synchronize()
     assert bool((y == 7).all())          # nothing was enqueued
-    n_ok = n - 1
-    assert c.ffn_workspace_bytes(n_ok, k) <= oes.FFN_NOALLOC_SCRATCH_BYTES
+    y_na = torch.empty((n_ok, H), dtype=torch.int16, device=dev)
+    y_ref = torch.empty_like(y_na)
+    ws = torch.empty(c.ffn_workspace_bytes(n_ok, k), dtype=torch.uint8, device=dev)
+    c.expert_ffn(x[:n_ok], slot_ids[:n_ok], w[:n_ok], y_ref, ws)
+    c.expert_ffn_noalloc(x[:n_ok], slot_ids[:n_ok], w[:n_ok], y_na)
+    torch.cuda.synchronize()
+    c.check()
+    assert torch.equal(y_na, y_ref)
     c.close()
