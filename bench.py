@@ -619,7 +619,7 @@ def _ffn_cold(w, cache, hb, host, sc, probes, log, launches=64):
         row = {"what": f"ffn bs={bs}", "bs": bs, "unique_experts": u, "bytes": nbytes, "avg_ms": ms,
                "GBps": nbytes / (ms * 1e6), "frac_of_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
                "disjoint_sets": R, "launches": launches, **paths,
-               "traffic": _pmc_traffic(f"expert_ffn_{w.fmt}_bs{bs}" if bs > 1 else f"expert_ffn_{w.fmt}")}
+               "traffic": _pmc_traffic(f"expert_ffn_{w.name}_bs{bs}" if bs > 1 else f"expert_ffn_{w.name}")}
         if probes:
             row["frac_of_measured_hbm_read"] = row["GBps"] / probes["hbm_read_GBps"]
         # the last launch ran on layer (launches - 1) % R's slots: check it against the oracle
