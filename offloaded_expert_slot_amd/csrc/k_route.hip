@@ -3,7 +3,7 @@
 // The pages name the top-k of each MoE layer (FreeToken MoE benchmark guide §4.3
 // routes bs * topk experts per step) but not the router; this is the plain one.
 //
-// Two launches, each one memory round trip deep:
+// Two launches, each one memory round trip deep (one for small routers, below):
 //   route_partial  - split-K GEMV: workgroup s sums rows [s*R, (s+1)*R) of
 //                    Wg [H, E] (bf16, row-major) against every token, fp32,
 //                    writing partial[s][t][e]; each thread owns one column octet
@@ -14,7 +14,9 @@
 //                    rank (experts with a larger logit, or an equal one at a
 //                    lower index) picks the top-k in order; one wave takes the
 //                    softmax over the chosen logits.
-// route_logits runs route_finish alone on given logits (one split).
+// route_logits runs route_finish alone on given logits (one split).  When Wg fits
+// one split (small routers), route_single does both in one launch: one workgroup
+// per token computes its logits and takes the top-k.
 
 #include <math.h>
 
@@ -121,14 +123,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_partial_kernel(const uint
 // result is deterministic).  Then the top-k by rank (larger logit first, lower
 // index on ties); lane j of wave 0 takes the j-th pick and writes its id and
 // renormalised weight.
+struct FinishSmem {
+  float zsum[kRouteThreads];
+  float z[512];
+  float top_v[32];
+  int top_i[32];
+  __align__(16) uint64_t rkey[512 + 2];
+  int rcnt[512];
+};
+
+__device__ __forceinline__ void finish_topk(FinishSmem &sm, int t, int E, int k, int32_t *ids, float *w);
+
 __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float *partial, int splits, int n, int E,
                                                                      int k, float *logits, int32_t *ids, float *w) {
-  __shared__ float zsum[kRouteThreads];
-  __shared__ float z[512];
-  __shared__ float top_v[32];
-  __shared__ int top_i[32];
-  __shared__ __align__(16) uint64_t rkey[512 + 2];
-  __shared__ int rcnt[512];
+  __shared__ FinishSmem sm;
+  float *zsum = sm.zsum, *z = sm.z;
   const int t = blockIdx.x;
   const int64_t stride = (int64_t)n * E;
   const int per = kRouteThreads / E >= 1 ? kRouteThreads / E : 1;   // threads per expert (E <= 256)
@@ -174,6 +183,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float
     }
   }
   __syncthreads();
+  finish_topk(sm, t, E, k, ids, w);
+}
+
+// The top-k of the logits sm.z[0, E) of token t (all threads of the workgroup;
+// sm.z written and synchronised by the caller).
+__device__ __forceinline__ void finish_topk(FinishSmem &sm, int t, int E, int k, int32_t *ids, float *w) {
+  float *z = sm.z, *top_v = sm.top_v;
+  int *top_i = sm.top_i, *rcnt = sm.rcnt;
+  uint64_t *rkey = sm.rkey;
   // top-k by rank: expert e's rank is the number of experts that beat it - a larger
   // logit, or an equal one at a lower index; a NaN logit is beaten by every number
   // and NaNs among themselves go by index.  Each expert gets one 64-bit key that
@@ -234,6 +252,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(const float
   }
 }
 
+// Routing in one launch when Wg fits one split (H <= the rows of a split, as for
+// small routers): one workgroup per token computes its logits and takes the top-k.
+// Thread (part, e) sums rows part, part + parts, ... of column e in fp32; the parts
+// are added in a fixed order through LDS.
+__global__ __launch_bounds__(kRouteThreads) void route_single_kernel(const uint16_t *x, const uint16_t *wg, int H,
+                                                                     int E, int k, float *logits, int32_t *ids,
+                                                                     float *w) {
+  __shared__ FinishSmem sm;
+  const int t = blockIdx.x;
+  const int parts = kRouteThreads / E;  // E <= 256
+  const int e = threadIdx.x % E, part = threadIdx.x / E;
+  float s = 0.f;
+  if (part < parts)
+    for (int h = part; h < H; h += parts) s = fmaf(bf16f(x[(int64_t)t * H + h]), bf16f(wg[(int64_t)h * E + e]), s);
+  sm.zsum[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < E) {
+    float tot = 0.f;
+    for (int q = 0; q < parts; ++q) tot += sm.zsum[q * E + threadIdx.x];
+    sm.z[threadIdx.x] = tot;
+    if (logits) logits[(int64_t)t * E + threadIdx.x] = tot;
+  }
+  __syncthreads();
+  finish_topk(sm, t, E, k, ids, w);
+}
+
 }  // namespace
 
 int route_splits(int H, int E) { return route_geom(H, E).splits; }
@@ -241,6 +285,10 @@ int route_splits(int H, int E) { return route_geom(H, E).splits; }
 hipError_t launch_route(const uint16_t *x, const uint16_t *wg, int n, int H, int E, int k, int32_t *ids, float *w,
                         float *logits, float *partial, hipStream_t s) {
   const RouteGeom geo = route_geom(H, E);
+  if (geo.splits == 1 && E <= kRouteThreads) {
+    hipLaunchKernelGGL(route_single_kernel, dim3(n), dim3(kRouteThreads), 0, s, x, wg, H, E, k, logits, ids, w);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_partial_kernel, dim3(geo.splits), dim3(kRouteThreads), 0, s, x, wg, n, H, E, geo, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -377,8 +377,11 @@ def test_load_rows_and_sdma_mode():
 
 
 # ------------------------------------------------------------------ route
+# (1, 256, 16, 2), (4, 256, 16, 2), (2, 96, 8, 8), (3, 128, 256, 8) and (7, 200, 64, 4) fit
+# one split of Wg and take the single-launch router; the others the split-K one
 @pytest.mark.parametrize("n,H,E,k", [(1, 256, 16, 2), (4, 256, 16, 2), (3, 2048, 128, 8), (33, 7168, 256, 8), (40, 2048, 24, 3),
-                                     (5, 4096, 256, 8), (2, 96, 8, 8), (9, 512, 512, 32), (1, 7168, 256, 8)])
+                                     (5, 4096, 256, 8), (2, 96, 8, 8), (9, 512, 512, 32), (1, 7168, 256, 8),
+                                     (3, 128, 256, 8), (7, 200, 64, 4)])
 def test_route_matches_oracle(n, H, E, k):
     _case(f"route n={n} H={H} E={E} k={k}")
     x = synth.activations(n, H, 0, "route").to(G.dev())
